@@ -1,0 +1,136 @@
+"""The fused FP8 block-quantized MoE layer forward, computed literally.
+
+Test infrastructure (see the package docstring).
+
+Sources (vLLM quantization / MoE pages):
+  * overview page, "FusedMoE Class": expert weights w13 (gate+up) and w2
+    (down) stored [num_experts, N, K]; a top-K router.
+  * overview page, "Modular Kernel Architecture": inputs are quantized and
+    dispatched, the expert GEMMs run as permute -> GEMM -> unpermute, and the
+    results are gathered.
+  * overview page, "Triton Fused MoE Kernel": per-block sorted tokens of one
+    expert; float32 dequantisation of the quantized accumulation, then the
+    optional router-weight multiply.
+  * overview page, "Weight Scale Granularities" and the fp8 oracle page's
+    quant keys: static 128x128 block weight scales, dynamic per-token
+    128-group activation scales, symmetric.
+The layer definition adds the activation (SiLU of the gate half times the up
+half), the requantisation of that product, and the weighted combine.
+
+Definition, with T tokens, hidden H, intermediate I, E experts, k slots,
+pair p = t * k + j routed to expert e = ids[t, j]:
+  1. (ids, w) = router.topk_softmax(logits, k, renormalize)
+  2. (xq, xs) = quant.per_token_group_quant(x);  Xf = dec(xq) * xs   (float64)
+  3. W13f[e] = dec(w13[e]) * w13_scale[e] (block-broadcast, float64), same for W2f
+  4. h[p, :] = W13f[e] @ Xf[t]              (float64 matmul), n in [0, 2I)
+  5. a[p, i] = silu(h[p, i]) * h[p, I + i]  (rows [0, I) of w13 are the gate,
+                                             [I, 2I) the up projection),
+     silu(z) = z / (1 + exp(-z)); computed in float64 and rounded to float32,
+     the precision in which the requantisation decides its codes
+  6. (aq, as) = quant.per_token_group_quant(a)   (group 128 along I)
+  7. y[p, :] = W2f[e] @ (dec(aq[p]) * as[p])     (float64 matmul)
+  8. out[t, :] = bf16_RNE( sum over j in slot order of w[t, j] * y[t*k+j, :] )
+                 summed in float64.
+Scale application per 128-wide K block followed by a float32 accumulation
+(the way the kernels order it) is the same sum as steps 4 and 7 up to
+rounding order.
+
+Parity: routing ids, the sorted layout and the codes/scales of step 2 are
+exact targets.  Step 6 codes depend on the accumulation order of steps 4-5,
+so they are a diagnostic, not an exact target.  The whole-layer output is
+pinned by the special cases in tests/test_oracle_moe.py (E = 1, k = 1 equals
+an independently written dense gated MLP; a scalar-loop brute force on a
+tiny layer; token-permutation equivariance; the renormalisation identity; a
+loose agreement with the unquantized float64 MLP).  The pages print no
+numeric example of the layer, so no end-to-end value is pinned to them.
+"""
+
+import numpy as np
+
+from . import e4m3, quant, router
+
+
+def bf16_round(v) -> np.ndarray:
+    """float64 -> nearest bfloat16 (ties to even), returned as float32.
+    Valid for the normal bf16 range, which is all the layer produces."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                        # v = m * 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # keep 8 significant bits
+    return r.astype(np.float32)
+
+
+def bf16_bits(v32) -> np.ndarray:
+    """float32 array holding bf16 values -> uint16 bf16 bit patterns."""
+    return (np.ascontiguousarray(v32, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x_rows, w13_e, w13s_e, w2_e, w2s_e):
+    """Steps 2-7 for rows that all go to one expert.
+    x_rows float32 [n, H] (bf16 values).  Returns dict of per-row tensors."""
+    x_rows = np.asarray(x_rows, dtype=np.float32)
+    I = w2_e.shape[1]
+    xq, xs = quant.per_token_group_quant(x_rows)
+    Xf = quant.dequant(xq, xs)
+    W13f = quant.block_dequant(w13_e, w13s_e)
+    h = Xf @ W13f.T                                       # [n, 2I] float64
+    a = (silu(h[:, :I]) * h[:, I:]).astype(np.float32)    # [n, I]
+    aq, as_ = quant.per_token_group_quant(a)
+    Af = quant.dequant(aq, as_)
+    W2f = quant.block_dequant(w2_e, w2s_e)
+    y = Af @ W2f.T                                        # [n, H] float64
+    return {"xq": xq, "xs": xs, "h": h, "a": a, "aq": aq, "as": as_, "y": y}
+
+
+def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
+                renormalize: bool, tokens=None):
+    """Whole-layer forward.
+
+    x float32 [T, H] (bf16 values), logits float32 [T, E],
+    w13 uint8 [E, 2I, H], w13_scale float32 [E, 2I/128, H/128],
+    w2 uint8 [E, H, I], w2_scale float32 [E, H/128, I/128].
+    ``tokens`` optionally restricts the computation to a list of token rows
+    (each token's output depends only on its own row, so this gives the same
+    values as the full forward at those rows).
+
+    Returns (out float32 [n_tok, H] holding bf16 values, info dict with ids,
+    w, xq, xs and per-pair a, aq, as, y in pair order p = row * k + j)."""
+    x = np.asarray(x, dtype=np.float32)
+    logits = np.asarray(logits, dtype=np.float32)
+    if tokens is not None:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        x = x[tokens]
+        logits = logits[tokens]
+    T, H = x.shape
+    E = logits.shape[1]
+    I = w2.shape[2]
+    ids, w = router.topk_softmax(logits, top_k, renormalize)
+    xq, xs = quant.per_token_group_quant(x)
+
+    P = T * top_k
+    flat = ids.reshape(-1)
+    y = np.zeros((P, H), dtype=np.float64)
+    a = np.zeros((P, I), dtype=np.float32)
+    aq = np.zeros((P, I), dtype=np.uint8)
+    as_ = np.zeros((P, I // 128), dtype=np.float32)
+    for e in range(E):
+        pairs = np.nonzero(flat == e)[0]
+        if pairs.size == 0:
+            continue
+        r = expert_ffn(x[pairs // top_k], w13[e], w13_scale[e], w2[e], w2_scale[e])
+        y[pairs] = r["y"]
+        a[pairs] = r["a"]
+        aq[pairs] = r["aq"]
+        as_[pairs] = r["as"]
+
+    acc = np.zeros((T, H), dtype=np.float64)
+    for j in range(top_k):
+        acc += w[:, j:j + 1].astype(np.float64) * y[j::top_k]
+    out = bf16_round(acc)
+    info = {"ids": ids, "w": w, "xq": xq, "xs": xs, "a": a, "aq": aq,
+            "as": as_, "y": y}
+    return out, info

@@ -1,0 +1,192 @@
+"""Pins of the whole-layer oracle (oracle/moe.py).
+
+* a brute force with explicit loops: routing by full sort, quantisation with
+  the exhaustive-search encoder, and each GEMM written per 128-wide K block
+  with the block scales indexed explicitly (w_scale[e, n // 128, kb]),
+  decoding through torch's float8 conversion;
+* E = 1, k = 1 equals a dense gated MLP written as three dense matmuls;
+* permuting the tokens permutes the output;
+* out(renormalized) = out(raw softmax weights) / sum of the selected
+  probabilities, up to bf16 rounding;
+* a loose agreement with the unquantized float64 MLP on the same weights;
+* planted mistakes in the oracle fail the brute-force pin.
+"""
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax
+
+from oracle import moe, quant, router
+from synth import make_activations, make_weights
+from tests import _brute
+
+DEC = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _layer(T=3, H=256, I=256, E=4, k=2, seed=7, logits_kind="normal"):
+    w13, w13s, w2, w2s = make_weights(H, I, E, seed)
+    x, logits = make_activations(H, E, T, seed * 10, logits_kind)
+    return (x.float().numpy(), logits.numpy(), w13.numpy(), w13s.numpy(),
+            w2.numpy(), w2s.numpy())
+
+
+def _quant_row(row):
+    codes, scales = [], []
+    for g in range(len(row) // 128):
+        c, s = _brute.quant_group_scalar(row[128 * g:128 * (g + 1)])
+        codes += c
+        scales.append(s)
+    return np.array(codes, np.uint8), np.array(scales, np.float32)
+
+
+def _blocked_matvec(wq, ws, v):
+    """out[n] = sum_kb ws[n//128, kb] * sum_{kk in kb} dec(wq[n, kk]) * v[kk]"""
+    N, K = wq.shape
+    out = np.zeros(N)
+    for n in range(N):
+        acc = 0.0
+        for kb in range(K // 128):
+            seg = slice(128 * kb, 128 * kb + 128)
+            acc += float(ws[n // 128, kb]) * float(np.dot(DEC[wq[n, seg]], v[seg]))
+        out[n] = acc
+    return out
+
+
+def brute_layer(x, logits, w13, w13s, w2, w2s, k, renorm):
+    T, H = x.shape
+    E = logits.shape[1]
+    I = w2.shape[2]
+    out = np.zeros((T, H), np.float32)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+        p = softmax(logits[t].astype(np.float64))[order]
+        wts = (p / p.sum() if renorm else p).astype(np.float32)
+        xq, xs = _quant_row(x[t])
+        xhat = DEC[xq] * np.repeat(xs.astype(np.float64), 128)
+        acc = np.zeros(H)
+        for j, e in enumerate(order):
+            h = _blocked_matvec(w13[e], w13s[e], xhat)
+            g, u = h[:I], h[I:]
+            a = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+            aq, as_ = _quant_row(a)
+            ahat = DEC[aq] * np.repeat(as_.astype(np.float64), 128)
+            y = _blocked_matvec(w2[e], w2s[e], ahat)
+            acc += float(wts[j]) * y
+        out[t] = torch.from_numpy(acc).to(torch.bfloat16).to(torch.float32).numpy()
+    return out
+
+
+def _assert_close_bf16(a, b, exact_frac=0.99):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    np.testing.assert_allclose(a, b, rtol=2.0 ** -7, atol=1e-6)
+    assert np.mean(a == b) >= exact_frac
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_brute_force_layer(renorm):
+    x, logits, w13, w13s, w2, w2s = _layer()
+    out, info = moe.moe_forward(x, logits, w13, w13s, w2, w2s, 2, renorm)
+    ref = brute_layer(x, logits, w13, w13s, w2, w2s, 2, renorm)
+    _assert_close_bf16(out, ref)
+
+
+def test_single_expert_is_dense_gated_mlp():
+    x, logits, w13, w13s, w2, w2s = _layer(T=5, E=1, I=384)
+    out, _ = moe.moe_forward(x, logits, w13, w13s, w2, w2s, 1, True)
+    I = w2.shape[2]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    kron = lambda s: np.kron(s.astype(np.float64), np.ones((128, 128)))
+    W1 = DEC[w13[0, :I]] * kron(w13s[0, :I // 128])
+    W3 = DEC[w13[0, I:]] * kron(w13s[0, I // 128:])
+    W2 = DEC[w2[0]] * kron(w2s[0])
+    rows = []
+    for r in range(x.shape[0]):
+        q, s = _quant_row(x[r])
+        rows.append(DEC[q] * np.repeat(s.astype(np.float64), 128))
+    X = t(np.stack(rows))
+    g = X @ t(W1).T
+    u = X @ t(W3).T
+    A = (torch.nn.functional.silu(g) * u).to(torch.float32).numpy()
+    Ahat = np.stack([DEC[q] * np.repeat(s.astype(np.float64), 128)
+                     for q, s in map(_quant_row, A)])
+    Y = (t(Ahat) @ t(W2).T).to(torch.bfloat16).to(torch.float32).numpy()
+    _assert_close_bf16(out, Y)
+
+
+def test_token_permutation_equivariance():
+    x, logits, w13, w13s, w2, w2s = _layer(T=24, H=256, I=256, E=8, k=2, seed=3)
+    out, _ = moe.moe_forward(x, logits, w13, w13s, w2, w2s, 2, True)
+    perm = np.random.default_rng(0).permutation(24)
+    outp, _ = moe.moe_forward(x[perm], logits[perm], w13, w13s, w2, w2s, 2, True)
+    _assert_close_bf16(outp, out[perm], exact_frac=0.999)
+    # the token-subset mode gives the same rows as the full forward
+    sub, _ = moe.moe_forward(x, logits, w13, w13s, w2, w2s, 2, True, tokens=[5, 0, 17])
+    _assert_close_bf16(sub, out[[5, 0, 17]], exact_frac=0.999)
+
+
+def test_renormalisation_identity():
+    x, logits, w13, w13s, w2, w2s = _layer(T=16, E=8, k=3, seed=4)
+    on, _ = moe.moe_forward(x, logits, w13, w13s, w2, w2s, 3, True)
+    off, _ = moe.moe_forward(x, logits, w13, w13s, w2, w2s, 3, False)
+    ids, w_raw = router.topk_softmax(logits, 3, False)
+    S = w_raw.astype(np.float64).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(on, off / S, rtol=2.0 ** -7, atol=1e-6)
+
+
+def test_close_to_unquantized_mlp():
+    x, logits, w13, w13s, w2, w2s = _layer(T=16, H=512, I=512, E=4, k=2, seed=9)
+    out, info = moe.moe_forward(x, logits, w13, w13s, w2, w2s, 2, True)
+    ids, w = info["ids"], info["w"]
+    I = w2.shape[2]
+    ref = np.zeros_like(out, dtype=np.float64)
+    for e in range(4):
+        W13 = quant.block_dequant(w13[e], w13s[e])
+        W2 = quant.block_dequant(w2[e], w2s[e])
+        h = x.astype(np.float64) @ W13.T
+        y = (moe.silu(h[:, :I]) * h[:, I:]) @ W2.T
+        for j in range(2):
+            m = ids[:, j] == e
+            ref[m] += w[m, j:j + 1] * y[m]
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel < 0.05, rel
+
+
+def test_bf16_round():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -30, -2.5], np.float64)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+    ref[3] = 1.0 + 2 ** -7                        # above the tie: rounds up
+    assert moe.bf16_round(v).tolist() == ref.tolist()
+
+
+def _swap_gate_up(x_rows, w13_e, w13s_e, w2_e, w2s_e):
+    I = w2_e.shape[1]
+    return moe_real_ffn(x_rows, np.concatenate([w13_e[I:], w13_e[:I]]),
+                        np.concatenate([w13s_e[I // 128:], w13s_e[:I // 128]]), w2_e, w2s_e)
+
+
+moe_real_ffn = moe.expert_ffn
+
+
+@pytest.mark.parametrize("mutant", ["swap_gate_up", "no_router_weight",
+                                    "transposed_block_scales", "inverted_act_scale"])
+def test_planted_mistakes_fail_brute_force(mutant, monkeypatch):
+    if mutant == "swap_gate_up":
+        monkeypatch.setattr(moe, "expert_ffn", _swap_gate_up)
+    elif mutant == "no_router_weight":
+        real = router.topk_softmax
+        monkeypatch.setattr(router, "topk_softmax",
+                            lambda l, k, r: (real(l, k, r)[0], np.ones((l.shape[0], k), np.float32)))
+    elif mutant == "transposed_block_scales":
+        real_bd = quant.block_dequant
+        monkeypatch.setattr(quant, "block_dequant",
+                            lambda w, ws, block=128: real_bd(w, np.ascontiguousarray(ws[::-1, ::-1]), block))
+    else:
+        real_q = quant.per_token_group_quant
+        def inv(x, group=128):
+            q, s = real_q(x, group)
+            return q, (np.float32(1.0) / s).astype(np.float32)
+        monkeypatch.setattr(quant, "per_token_group_quant", inv)
+    with pytest.raises(AssertionError):
+        test_brute_force_layer(True)
