@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused FP8 block-quantized MoE forward on one MI355X.
+
+Workload (default "dsv3"): a DeepSeek-V3-shaped routed-expert layer, H=7168,
+I=2048, E=256, top_k=8 softmax routing with renormalisation and a seeded
++-0.5 per-expert logit bias (load skew), FP8 e4m3fn weights with 128x128
+block scales (~11.3 GB, drawn N(0, 0.02)), bf16 activations N(0, 1) with
+dynamic per-token 128-group quantisation.  One step = one decode batch of
+T=64 tokens plus one prefill batch of T=8192 tokens through the whole path
+(router, sort-and-pad, activation quant, GEMM1 + SiLU*mul + requant, GEMM2 +
+routing weight, combine).  Inputs are resident in HBM before timing starts.
+The standalone activation quantiser is also timed on its own workload, bf16
+[16384, 7168] with 1% x100 outliers.
+
+Prints one JSON line.  value = tokens per second over the step.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused FP8 MoE tokens/s + % of HBM/MFMA roofline, decode M=64 & prefill M=8192"
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_FP8_PEAK = 5.0e15     # dense FP8 FLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dsv3", choices=["dsv3", "mixtral", "qwen3", "tiny"])
+    p.add_argument("--cpu-sample-tokens", type=int, default=4)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def batch_sizes(name):
+    from synth import MOE_WORKLOADS
+    t = MOE_WORKLOADS[name]["T"]
+    return (min(t), max(t)) if len(t) > 1 else (t[0], t[0])
+
+
+def algorithmic(ids, T, H, I, E, k):
+    """Bytes and FLOPs the method must move / compute (no padding, no
+    intermediates), per stage and for the layer."""
+    import numpy as np
+    P = T * k
+    active = int(np.unique(ids).size)
+    w13_b = active * (2 * I * H + 4 * (2 * I // 128) * (H // 128))
+    w2_b = active * (H * I + 4 * (H // 128) * (I // 128))
+    a_b = P * I + 4 * P * (I // 128)
+    return {
+        "active_experts": active,
+        "layer_bytes": w13_b + w2_b + 2 * T * H + 2 * T * H + 4 * T * E,
+        "layer_flops": 6 * P * H * I,
+        "stage": {
+            "router": (4 * T * E + 8 * P, 0),
+            "align": (8 * P, 0),
+            "quant": (2 * T * H + T * H + 4 * T * (H // 128), 0),
+            "gemm1": (w13_b + T * H + 4 * T * (H // 128) + a_b, 4 * P * H * I),
+            "gemm2": (w2_b + a_b + 4 * P + 2 * P * H, 2 * P * H * I),
+            "combine": (2 * P * H + 2 * T * H, 0),
+        },
+    }
+
+
+def roofline_of(nbytes, flops, seconds):
+    t_hbm, t_mfma = nbytes / HBM_PEAK, flops / MFMA_FP8_PEAK
+    if t_mfma > t_hbm:
+        a = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": MFMA_FP8_PEAK / 1e12, "unit": "TFLOP/s",
+                "frac": a / (MFMA_FP8_PEAK / 1e12)}
+    a = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": a / (HBM_PEAK / 1e9)}
+
+
+def cpu_baseline(w, x_dec, logits_dec, k, n_tok):
+    """The oracle, as it stands, on the first n_tok tokens of the decode batch."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe as ref_moe
+    from oracle import router as ref_router
+    logits = logits_dec[:n_tok].cpu().numpy()
+    x = x_dec[:n_tok].float().cpu().numpy()
+    ids, _ = ref_router.topk_softmax(logits, k, True)
+    experts = np.unique(ids)
+    sel = torch.from_numpy(experts).cuda()
+    E = w["w13"].shape[0]
+    w13 = np.zeros((E,) + tuple(w["w13"].shape[1:]), np.uint8)
+    w2 = np.zeros((E,) + tuple(w["w2"].shape[1:]), np.uint8)
+    w13[experts] = w["w13"][sel].cpu().numpy()
+    w2[experts] = w["w2"][sel].cpu().numpy()
+    w13s, w2s = w["w13_scale"].cpu().numpy(), w["w2_scale"].cpu().numpy()
+    t0 = time.perf_counter()
+    ref_moe.moe_forward(x, logits, w13, w13s, w2, w2s, k, True)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_tok} tokens of the T=64 decode batch ({experts.size} experts, "
+                      f"{n_tok * k} token-expert pairs), float64 dequantised GEMMs; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built and measured on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fp8_block_quantized_amd as moe
+    from synth import MOE_WORKLOADS, make_activations, make_weights, quant_input
+
+    moe.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = MOE_WORKLOADS[args.workload]
+    H, I, E, k = c["H"], c["I"], c["E"], c["top_k"]
+    base = 1000 * c["index"]
+    T_dec, T_pre = batch_sizes(args.workload)
+    w13, w13s, w2, w2s = make_weights(H, I, E, base + 2, dev)
+    wts = {"w13": w13, "w13_scale": w13s, "w2": w2, "w2_scale": w2s}
+    phases = {}
+    for name, T in (("decode", T_dec), ("prefill", T_pre)):
+        x, logits = make_activations(H, E, T, base, c["logits"], dev)
+        phases[name] = {"T": T, "x": x, "logits": logits,
+                        "ws": moe.alloc_workspace(T, H, I, E, k, dev),
+                        "out": torch.empty((T, H), dtype=torch.bfloat16, device=dev)}
+    order = ["decode", "prefill"] if T_dec != T_pre else ["decode"]
+
+    def run(ph, events=None):
+        moe.moe_fp8_forward(ph["x"], ph["logits"], w13, w13s, w2, w2s, k, True,
+                            out=ph["out"], workspace=ph["ws"], events=events)
+
+    for _ in range(args.warmup):
+        for n in order:
+            run(phases[n])
+    torch.cuda.synchronize()
+
+    nst = len(moe.STAGES)
+    evs = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+               for _ in range(args.steps)] for n in order}
+    for n in order:
+        for lst in evs[n]:
+            for e in lst:
+                e.record()          # creates the HIP events
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for n in order:
+            run(phases[n], evs[n][s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    result_phases = {}
+    kernels = {}
+    for n in order:
+        ph = phases[n]
+        T = ph["T"]
+        taps = moe.workspace_taps(ph["ws"], T, H, I, E, k)
+        alg = algorithmic(taps["topk_ids"].cpu().numpy(), T, H, I, E, k)
+        st_ms = np.array([[evs[n][s][i].elapsed_time(evs[n][s][i + 1]) for i in range(nst)]
+                          for s in range(args.steps)]).mean(axis=0)
+        layer_ms = float(st_ms.sum())
+        lb, lf = alg["layer_bytes"], alg["layer_flops"]
+        result_phases[n] = {
+            "T": T, "ms": layer_ms, "tokens_per_s": T / (layer_ms * 1e-3),
+            "active_experts": alg["active_experts"],
+            "alg_bytes": lb, "alg_flops": lf,
+            "hbm_frac": lb / (layer_ms * 1e-3) / HBM_PEAK,
+            "mfma_frac": lf / (layer_ms * 1e-3) / MFMA_FP8_PEAK,
+            "stage_ms": {s: float(v) for s, v in zip(moe.STAGES, st_ms)},
+        }
+        for s, v in zip(moe.STAGES, st_ms):
+            b, f = alg["stage"][s]
+            kernels[f"{n}.{s}"] = {"ms": float(v), "bytes": b, "flops": f}
+
+    # standalone activation quantiser, rotating three input buffers (> MALL)
+    from synth import QUANT_WORKLOAD
+    M, K = QUANT_WORKLOAD["M"], QUANT_WORKLOAD["K"]
+    xq_in = [quant_input(device=dev, seed_base=4000 + 10 * i) for i in range(3)]
+    q_out = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(3)]
+    s_out = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(3)]
+    for i in range(3):
+        moe.per_token_group_quant_fp8(xq_in[i], q=q_out[i], scales=s_out[i])
+    qe = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        qe[2 * s].record()
+        moe.per_token_group_quant_fp8(xq_in[s % 3], q=q_out[s % 3], scales=s_out[s % 3])
+        qe[2 * s + 1].record()
+    torch.cuda.synchronize()
+    q_ms = float(np.mean([qe[2 * s].elapsed_time(qe[2 * s + 1]) for s in range(args.steps)]))
+    q_bytes = 2 * M * K + M * K + 4 * M * (K // 128)
+    quant = {"M": M, "K": K, "ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
+             "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
+
+    dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
+    dom = kernels[dom_name]
+    roof = roofline_of(dom["bytes"], dom["flops"], dom["ms"] * 1e-3)
+    roof.update({"kernel": dom_name, "traffic": None,
+                 "alg_bytes_per_launch": dom["bytes"], "alg_flops_per_launch": dom["flops"],
+                 "ms_per_launch": dom["ms"]})
+
+    tokens = sum(phases[n]["T"] for n in order)
+    ms_step = wall / args.steps * 1e3
+    out = {
+        "metric": METRIC, "value": tokens / (wall / args.steps), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp8e4m3 -> f32 accumulate (bf16 in/out)", "data": "synthetic",
+        "config": {"workload": f"{args.workload}-shaped MoE layer H={H} I={I} E={E} top_k={k}, "
+                               f"decode T={T_dec} + prefill T={T_pre} per step",
+                   "H": H, "I": I, "E": E, "top_k": k, "T_decode": T_dec, "T_prefill": T_pre,
+                   "block_m": {n: moe.moe_fp8_block_m(phases[n]["T"], H, I, E, k) for n in order}},
+        "roofline": roof,
+        "phases": result_phases,
+        "quant_standalone": quant,
+    }
+    if not args.no_cpu_baseline:
+        ph = phases["decode"]
+        out["cpu_baseline"] = cpu_baseline(wts, ph["x"], ph["logits"], k, args.cpu_sample_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

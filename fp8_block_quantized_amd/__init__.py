@@ -1,0 +1,228 @@
+"""Python binding of libmoe_fp8.so, the gfx950 fused FP8 block-quantized MoE
+library.  Argument marshalling only: every step of the computation runs in
+the HIP kernels behind the C ABI declared in include/moe_fp8.h.  torch is
+used for device memory and streams.  There is no fallback: if the shared
+library is missing or a tensor is not a contiguous GPU tensor of the right
+type, the call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_fp8.so")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
+          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIAS"}
+TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "xq", "xs",
+        "aq", "as", "y", "align_scratch"]
+MAX_EXPERTS = 512
+MAX_TOKENS = 16384
+MAX_TOP_K = 32
+QUANT_GROUP = 128
+
+STAGES = ["router", "align", "quant", "gemm1", "gemm2", "combine"]
+
+EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layout",
+           "moe_fp8_forward", "moe_fp8_forward_traced", "per_token_group_quant_fp8", "moe_topk_softmax",
+           "moe_align_scratch_bytes", "moe_align", "moe_status_string"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    c_int, c_size, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    lib.moe_fp8_block_m.argtypes = [c_int] * 5
+    lib.moe_fp8_block_m.restype = c_int
+    lib.moe_fp8_workspace_bytes.argtypes = [c_int] * 5
+    lib.moe_fp8_workspace_bytes.restype = c_size
+    lib.moe_fp8_workspace_layout.argtypes = [c_int] * 5 + [ctypes.POINTER(c_size)]
+    lib.moe_fp8_workspace_layout.restype = c_int
+    lib.moe_fp8_forward.argtypes = [vp] * 6 + [c_int] * 6 + [vp, vp, c_size, vp]
+    lib.moe_fp8_forward.restype = c_int
+    lib.moe_fp8_forward_traced.argtypes = [vp] * 6 + [c_int] * 6 + [vp, vp, c_size, vp,
+                                                                   ctypes.POINTER(vp)]
+    lib.moe_fp8_forward_traced.restype = c_int
+    lib.per_token_group_quant_fp8.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
+    lib.per_token_group_quant_fp8.restype = c_int
+    lib.moe_topk_softmax.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp]
+    lib.moe_topk_softmax.restype = c_int
+    lib.moe_align_scratch_bytes.argtypes = [c_int] * 3
+    lib.moe_align_scratch_bytes.restype = c_size
+    lib.moe_align.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]
+    lib.moe_align.restype = c_int
+    lib.moe_status_string.argtypes = [c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def moe_fp8_block_m(T, H, I, E, top_k):
+    r = load_library().moe_fp8_block_m(T, H, I, E, top_k)
+    _check("moe_fp8_block_m", r if r < 0 else 0)
+    return r
+
+
+def moe_fp8_workspace_bytes(T, H, I, E, top_k):
+    return load_library().moe_fp8_workspace_bytes(T, H, I, E, top_k)
+
+
+def moe_fp8_workspace_layout(T, H, I, E, top_k):
+    offs = (ctypes.c_size_t * len(TAPS))()
+    _check("moe_fp8_workspace_layout",
+           load_library().moe_fp8_workspace_layout(T, H, I, E, top_k, offs))
+    return dict(zip(TAPS, list(offs)))
+
+
+def alloc_workspace(T, H, I, E, top_k, device="cuda"):
+    n = moe_fp8_workspace_bytes(T, H, I, E, top_k)
+    if n == 0:
+        raise MoeError("moe_fp8_workspace_bytes", -2)
+    return torch.empty(n, dtype=torch.uint8, device=device)   # caching allocator: 512-B aligned
+
+
+def moe_fp8_forward(x, router_logits, w13, w13_scale, w2, w2_scale, top_k, renormalize,
+                    out=None, workspace=None, stream=None, events=None):
+    """Fused FP8 MoE forward.  x bf16 [T, H], router_logits f32 [T, E],
+    w13 uint8 [E, 2I, H], w13_scale f32 [E, 2I/128, H/128], w2 uint8 [E, H, I],
+    w2_scale f32 [E, H/128, I/128].  Returns out bf16 [T, H].
+    With ``events`` (len(STAGES) + 1 timing-enabled torch.cuda.Event objects
+    that have been recorded once), calls moe_fp8_forward_traced, which records
+    them around each stage on the launch stream."""
+    T, H = x.shape
+    E = router_logits.shape[1]
+    I = w2.shape[2]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, I, E, top_k, x.device)
+    args = [_dev(x, torch.bfloat16, "x"), _dev(router_logits, torch.float32, "router_logits"),
+            _dev(w13, torch.uint8, "w13"), _dev(w13_scale, torch.float32, "w13_scale"),
+            _dev(w2, torch.uint8, "w2"), _dev(w2_scale, torch.float32, "w2_scale"),
+            T, H, I, E, int(top_k), int(bool(renormalize)),
+            _dev(out, torch.bfloat16, "out"), _dev(workspace, torch.uint8, "workspace"),
+            workspace.numel(), _stream(stream)]
+    lib = load_library()
+    if events is None:
+        _check("moe_fp8_forward", lib.moe_fp8_forward(*args))
+    else:
+        if len(events) != len(STAGES) + 1:
+            raise ValueError(f"need {len(STAGES) + 1} events")
+        handles = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+        _check("moe_fp8_forward_traced", lib.moe_fp8_forward_traced(*args, handles))
+    return out
+
+
+def workspace_taps(workspace, T, H, I, E, top_k):
+    """Views of the forward's intermediates inside its workspace."""
+    off = moe_fp8_workspace_layout(T, H, I, E, top_k)
+    bm = moe_fp8_block_m(T, H, I, E, top_k)
+    P = T * top_k
+    cap = -(-(P + E * (bm - 1)) // bm) * bm
+
+    def view(name, dtype, shape):
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return workspace[off[name]:off[name] + nbytes].view(dtype).view(shape)
+
+    return {
+        "block_m": bm, "cap": cap,
+        "topk_ids": view("topk_ids", torch.int32, (T, top_k)),
+        "topk_weights": view("topk_weights", torch.float32, (T, top_k)),
+        "sorted_ids": view("sorted_ids", torch.int32, (cap,)),
+        "expert_ids": view("expert_ids", torch.int32, (cap // bm,)),
+        "ntpp": view("ntpp", torch.int32, (1,)),
+        "xq": view("xq", torch.uint8, (T, H)),
+        "xs": view("xs", torch.float32, (T, H // 128)),
+        "aq": view("aq", torch.uint8, (cap, I)),
+        "as": view("as", torch.float32, (cap, I // 128)),
+        "y": view("y", torch.bfloat16, (P, H)),
+    }
+
+
+def per_token_group_quant_fp8(x, group_size=128, q=None, scales=None, stream=None):
+    """x bf16 [M, K] -> (q uint8 e4m3fn codes [M, K], scales f32 [M, K/group])."""
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // group_size), dtype=torch.float32, device=x.device)
+    st = load_library().per_token_group_quant_fp8(
+        _dev(x, torch.bfloat16, "x"), M, K, group_size, _dev(q, torch.uint8, "q"),
+        _dev(scales, torch.float32, "scales"), _stream(stream))
+    _check("per_token_group_quant_fp8", st)
+    return q, scales
+
+
+def moe_topk_softmax(logits, top_k, renormalize, ids=None, weights=None, stream=None):
+    """logits f32 [T, E] -> (ids int32 [T, k], weights f32 [T, k])."""
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    st = load_library().moe_topk_softmax(
+        _dev(logits, torch.float32, "logits"), T, E, int(top_k), int(bool(renormalize)),
+        _dev(ids, torch.int32, "ids"), _dev(weights, torch.float32, "weights"), _stream(stream))
+    _check("moe_topk_softmax", st)
+    return ids, weights
+
+
+def moe_align(topk_ids, num_experts, block_m, stream=None):
+    """topk_ids int32 [T, k] -> (sorted_ids, expert_ids, num_tokens_post_padded)
+    over the full capacity; only the first num_tokens_post_padded rows are defined."""
+    T, k = topk_ids.shape
+    P = T * k
+    cap = -(-(P + num_experts * (block_m - 1)) // block_m) * block_m
+    dev = topk_ids.device
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
+    ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+    lib = load_library()
+    nscr = lib.moe_align_scratch_bytes(T, k, num_experts)
+    scratch = torch.empty(max(nscr, 4), dtype=torch.uint8, device=dev)
+    st = lib.moe_align(_dev(topk_ids, torch.int32, "topk_ids"), T, k, num_experts, block_m,
+                       _dev(sorted_ids, torch.int32, "sorted_ids"),
+                       _dev(expert_ids, torch.int32, "expert_ids"), _dev(ntpp, torch.int32, "ntpp"),
+                       _dev(scratch, torch.uint8, "scratch"), scratch.numel(), _stream(stream))
+    _check("moe_align", st)
+    return sorted_ids, expert_ids, ntpp

@@ -1,0 +1,133 @@
+// Sort-and-pad of routed pairs by expert ("moe_align").
+//
+// Operation (overview page, "Triton Fused MoE Kernel": each program block
+// takes BLOCK_SIZE_M sorted tokens of one expert): the P = T*top_k pairs
+// p = t*top_k + j are grouped by expert in ascending p, each expert's run is
+// padded with the sentinel P to a multiple of block_m, and every block of
+// block_m rows records its expert.
+//
+// A deterministic three-kernel counting sort, no host synchronisation and no
+// global atomics:
+//   1. count:   each 1024-pair chunk builds its per-expert histogram in LDS.
+//   2. scan:    one workgroup turns the chunk histograms into padded expert
+//               offsets, the base of every (chunk, expert) run, the block ->
+//               expert table, the sentinels and the padded total.
+//   3. scatter: each chunk ranks its pairs stably inside their expert (a
+//               ballot match inside each wave plus per-wave counts in LDS)
+//               and writes them to base + rank.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kChunk = 1024;
+constexpr int kMaxE = 512;
+
+__global__ __launch_bounds__(1024) void align_count_kernel(const int32_t* __restrict__ ids, int P,
+                                                           int E, int32_t* __restrict__ counts) {
+  __shared__ int hist[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kChunk) hist[e] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * kChunk + threadIdx.x;
+  if (p < P) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);   // ids outside [0, E) are dropped
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kChunk) counts[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(1024) void align_scan_kernel(
+    const int32_t* __restrict__ counts, int nchunk, int E, int BM, int P,
+    int32_t* __restrict__ base, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp) {
+  __shared__ int scan[kChunk];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int b = 0; b < nchunk; ++b) total += counts[(size_t)b * E + e];
+  const int pad = (total + BM - 1) / BM * BM;
+  scan[e] = pad;
+  __syncthreads();
+  for (int off = 1; off < kChunk; off <<= 1) {
+    const int v = e >= off ? scan[e - off] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int incl = scan[e];
+  const int excl = incl - pad;
+  const int padded_total = scan[kChunk - 1];
+  if (e == 0) ntpp[0] = padded_total;
+  if (e < E) {
+    int run = excl;
+    for (int b = 0; b < nchunk; ++b) {
+      base[(size_t)b * E + e] = run;
+      run += counts[(size_t)b * E + e];
+    }
+    for (int r = total; r < pad; ++r) sorted_ids[excl + r] = P;
+  }
+  // block -> expert: the expert whose padded run [excl, incl) holds the block
+  const int nblocks = padded_total / BM;
+  for (int blk = threadIdx.x; blk < nblocks; blk += kChunk) {
+    const int row = blk * BM;
+    int lo = 0, hi = E - 1;  // first expert with inclusive end > row
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (scan[mid] > row) hi = mid; else lo = mid + 1;
+    }
+    expert_ids[blk] = lo;
+  }
+}
+
+__global__ __launch_bounds__(1024) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int ebits, const int32_t* __restrict__ base,
+    int32_t* __restrict__ sorted_ids) {
+  __shared__ int wcnt[kChunk / 64][kMaxE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < (kChunk / 64) * E; i += kChunk) wcnt[i / E][i % E] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * kChunk + threadIdx.x;
+  const int e0 = p < P ? ids[p] : -1;
+  const bool valid = (unsigned)e0 < (unsigned)E;
+  const int e = valid ? e0 : 0;
+  unsigned long long peers = __ballot(valid);
+  for (int bit = 0; bit < ebits; ++bit) {
+    const bool b = (e >> bit) & 1;
+    const unsigned long long m = __ballot(b);
+    peers &= b ? m : ~m;
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const int rank_in_wave = __popcll(peers & below);
+  if (valid && rank_in_wave == 0) wcnt[wave][e] = __popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wcnt[w][e];
+    sorted_ids[base[(size_t)blockIdx.x * E + e] + before + rank_in_wave] = p;
+  }
+}
+
+size_t align_scratch_bytes(int P, int E) {
+  const size_t nchunk = ((size_t)P + kChunk - 1) / kChunk;
+  return 2 * nchunk * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
+                        int32_t* expert_ids, int32_t* ntpp, void* scratch, hipStream_t stream) {
+  const int nchunk = (P + kChunk - 1) / kChunk;
+  int32_t* counts = (int32_t*)scratch;
+  int32_t* base = counts + (size_t)nchunk * E;
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  if (nchunk > 0)
+    hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, P, E, counts);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kChunk), 0, stream, counts, nchunk, E, BM, P,
+                     base, sorted_ids, expert_ids, ntpp);
+  if (nchunk > 0)
+    hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, P, E, ebits,
+                       base, sorted_ids);
+  return hipGetLastError();
+}
+
+}  // namespace moe

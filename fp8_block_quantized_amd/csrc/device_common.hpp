@@ -1,0 +1,70 @@
+// Device helpers shared by the HIP kernels of the FP8 MoE library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 128;          // activation group and weight block edge
+constexpr float kFp8Max = 448.0f;    // largest finite e4m3fn magnitude
+constexpr float kAmaxEps = 1e-8f;    // lower clamp of a group amax
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Correctly rounded float32 quotient x / s given r = RN(1 / s), from one
+// product and two fused multiply-adds (Markstein's correction step: with r
+// the correctly rounded reciprocal and q0 within an ulp of x / s, the
+// remainder x - q0*s is exact and q0 + rem*r rounds to RN(x / s)).
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  float q0 = x * r;
+  float rem = __builtin_fmaf(-q0, s, x);
+  return __builtin_fmaf(rem, r, q0);
+}
+
+__device__ __forceinline__ float clamp_fp8(float v) {
+  return __builtin_fminf(__builtin_fmaxf(v, -kFp8Max), kFp8Max);
+}
+
+// Four float32 values (already within +-448) -> four e4m3fn codes, RNE, the
+// first value in the lowest byte.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Scale of a group from its amax: max(amax, 1e-8) / 448 with an IEEE
+// (correctly rounded) float32 division, and its correctly rounded reciprocal.
+__device__ __forceinline__ void group_scale(float amax, float& s, float& r) {
+  s = __builtin_fmaxf(amax, kAmaxEps) / kFp8Max;
+  r = 1.0f / s;
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int first_mask, int last_mask) {
+  for (int m = first_mask; m >= last_mask; m >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+// Hardware dispatches consecutive workgroup ids round-robin over the eight
+// XCDs.  Renumber them so that each XCD receives a contiguous range of
+// logical ids: tiles that share a weight panel then run on one XCD and meet
+// in its L2.  A bijection on [0, n) for any n.
+__device__ __forceinline__ int xcd_contiguous_id(int bid, int n) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int q = n >> 3, rem = n & 7;
+  return xcd * q + (xcd < rem ? xcd : rem) + slot;
+}
+
+}  // namespace moe

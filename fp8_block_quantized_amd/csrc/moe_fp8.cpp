@@ -1,0 +1,251 @@
+// C ABI of the FP8 MoE library: argument checks, workspace layout and the
+// launch sequence of the fused forward.  Every check runs on the host before
+// anything is enqueued; nothing here allocates or synchronises.
+#include "../../include/moe_fp8.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_moe_shape(int T, int H, int I, int E, int top_k) {
+  if (T < 1 || T > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
+  if (H < 128 || H % 128 || I < 128 || I % 128) return MOE_ERR_SHAPE;
+  if (H > (1 << 16) || I > (1 << 16)) return MOE_ERR_SHAPE;
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (top_k < 1 || top_k > E || top_k > MOE_MAX_TOP_K) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// Rows per expert block: the smallest power of two holding 1.5x the mean
+// number of pairs per expert, within [16, 128].  Decode batches get small
+// blocks (little padding, one block per expert); prefill batches get 128.
+int pick_block_m(int T, int E, int top_k) {
+  const long long P = (long long)T * top_k;
+  const double want = 1.5 * (double)P / (double)E;
+  int bm = 16;
+  while (bm < 128 && bm < want) bm <<= 1;
+  return bm;
+}
+
+struct Layout {
+  int BM;
+  size_t cap;
+  size_t off[MOE_TAP_COUNT];
+  size_t total;
+};
+
+void make_layout(int T, int H, int I, int E, int top_k, Layout& L) {
+  const size_t P = (size_t)T * top_k;
+  L.BM = pick_block_m(T, E, top_k);
+  L.cap = round_up(P + (size_t)E * (L.BM - 1), L.BM);
+  size_t sz[MOE_TAP_COUNT];
+  sz[MOE_TAP_TOPK_IDS] = P * 4;
+  sz[MOE_TAP_TOPK_WEIGHTS] = P * 4;
+  sz[MOE_TAP_SORTED_IDS] = L.cap * 4;
+  sz[MOE_TAP_EXPERT_IDS] = (L.cap / L.BM) * 4;
+  sz[MOE_TAP_NTPP] = 4;
+  sz[MOE_TAP_XQ] = (size_t)T * H;
+  sz[MOE_TAP_XS] = (size_t)T * (H / 128) * 4;
+  sz[MOE_TAP_AQ] = L.cap * I;
+  sz[MOE_TAP_AS] = L.cap * (I / 128) * 4;
+  sz[MOE_TAP_Y] = P * H * 2;
+  sz[MOE_TAP_ALIGN_SCRATCH] = moe::align_scratch_bytes((int)P, E);
+  size_t o = 0;
+  for (int i = 0; i < MOE_TAP_COUNT; ++i) {
+    L.off[i] = o;
+    o = round_up(o + sz[i], kAlign);
+  }
+  L.total = o;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or not a multiple of 128";
+    case MOE_ERR_UNSUPPORTED: return "request not supported by this library";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP runtime error at launch";
+    case MOE_ERR_ALIAS: return "an output overlaps an input or the workspace";
+    default: return "unknown status";
+  }
+}
+
+int moe_fp8_block_m(int T, int H, int I, int E, int top_k) {
+  const int st = check_moe_shape(T, H, I, E, top_k);
+  if (st != MOE_OK) return st;
+  return pick_block_m(T, E, top_k);
+}
+
+size_t moe_fp8_workspace_bytes(int T, int H, int I, int E, int top_k) {
+  if (check_moe_shape(T, H, I, E, top_k) != MOE_OK) return 0;
+  Layout L;
+  make_layout(T, H, I, E, top_k, L);
+  return L.total;
+}
+
+int moe_fp8_workspace_layout(int T, int H, int I, int E, int top_k,
+                             size_t offsets[MOE_TAP_COUNT]) {
+  if (!offsets) return MOE_ERR_NULL;
+  const int st = check_moe_shape(T, H, I, E, top_k);
+  if (st != MOE_OK) return st;
+  Layout L;
+  make_layout(T, H, I, E, top_k, L);
+  for (int i = 0; i < MOE_TAP_COUNT; ++i) offsets[i] = L.off[i];
+  return MOE_OK;
+}
+
+static int forward_impl(const void* x, const float* router_logits, const uint8_t* w13,
+                        const float* w13_scale, const uint8_t* w2, const float* w2_scale, int T,
+                        int H, int I, int E, int top_k, int renormalize, void* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        hipEvent_t* ev) {
+  if (!x || !router_logits || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace)
+    return MOE_ERR_NULL;
+  int st = check_moe_shape(T, H, I, E, top_k);
+  if (st != MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_SHAPE;
+  Layout L;
+  make_layout(T, H, I, E, top_k, L);
+  if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)x % 16 || (uintptr_t)out % 16 || (uintptr_t)w13 % 16 || (uintptr_t)w2 % 16 ||
+      (uintptr_t)router_logits % 4 || (uintptr_t)w13_scale % 4 || (uintptr_t)w2_scale % 4)
+    return MOE_ERR_UNSUPPORTED;
+  const size_t out_bytes = (size_t)T * H * 2;
+  const size_t w13_bytes = (size_t)E * 2 * I * H, w2_bytes = (size_t)E * H * I;
+  const size_t w13s_bytes = (size_t)E * (2 * I / 128) * (H / 128) * 4;
+  const size_t w2s_bytes = (size_t)E * (H / 128) * (I / 128) * 4;
+  if (overlaps(out, out_bytes, x, out_bytes) ||
+      overlaps(out, out_bytes, router_logits, (size_t)T * E * 4) ||
+      overlaps(out, out_bytes, w13, w13_bytes) || overlaps(out, out_bytes, w2, w2_bytes) ||
+      overlaps(out, out_bytes, w13_scale, w13s_bytes) ||
+      overlaps(out, out_bytes, w2_scale, w2s_bytes) ||
+      overlaps(out, out_bytes, workspace, L.total))
+    return MOE_ERR_ALIAS;
+
+  char* ws = (char*)workspace;
+  int32_t* ids = (int32_t*)(ws + L.off[MOE_TAP_TOPK_IDS]);
+  float* tw = (float*)(ws + L.off[MOE_TAP_TOPK_WEIGHTS]);
+  int32_t* sorted = (int32_t*)(ws + L.off[MOE_TAP_SORTED_IDS]);
+  int32_t* eids = (int32_t*)(ws + L.off[MOE_TAP_EXPERT_IDS]);
+  int32_t* ntpp = (int32_t*)(ws + L.off[MOE_TAP_NTPP]);
+  uint8_t* xq = (uint8_t*)(ws + L.off[MOE_TAP_XQ]);
+  float* xs = (float*)(ws + L.off[MOE_TAP_XS]);
+  uint8_t* aq = (uint8_t*)(ws + L.off[MOE_TAP_AQ]);
+  float* as = (float*)(ws + L.off[MOE_TAP_AS]);
+  uint16_t* y = (uint16_t*)(ws + L.off[MOE_TAP_Y]);
+  void* scratch = ws + L.off[MOE_TAP_ALIGN_SCRATCH];
+  const int P = T * top_k;
+  const int nblk = (int)(L.cap / L.BM);
+
+  hipError_t err;
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if (mark(0)) return MOE_ERR_HIP;
+  if ((err = moe::launch_topk_softmax(router_logits, T, E, top_k, renormalize, ids, tw, stream)))
+    return MOE_ERR_HIP;
+  if (mark(1)) return MOE_ERR_HIP;
+  if ((err = moe::launch_align(ids, P, E, L.BM, sorted, eids, ntpp, scratch, stream)))
+    return MOE_ERR_HIP;
+  if (mark(2)) return MOE_ERR_HIP;
+  if ((err = moe::launch_group_quant(x, T, H, xq, xs, stream))) return MOE_ERR_HIP;
+  if (mark(3)) return MOE_ERR_HIP;
+  if ((err = moe::launch_gemm1(xq, xs, w13, w13_scale, sorted, eids, ntpp, H, I, P, top_k, L.BM,
+                               nblk, aq, as, stream)))
+    return MOE_ERR_HIP;
+  if (mark(4)) return MOE_ERR_HIP;
+  if ((err = moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, tw, H, I, P, L.BM, nblk,
+                               y, stream)))
+    return MOE_ERR_HIP;
+  if (mark(5)) return MOE_ERR_HIP;
+  if ((err = moe::launch_combine(y, T, H, top_k, (uint16_t*)out, stream))) return MOE_ERR_HIP;
+  if (mark(6)) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_fp8_forward(const void* x, const float* router_logits, const uint8_t* w13,
+                    const float* w13_scale, const uint8_t* w2, const float* w2_scale, int T,
+                    int H, int I, int E, int top_k, int renormalize, void* out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(x, router_logits, w13, w13_scale, w2, w2_scale, T, H, I, E, top_k,
+                      renormalize, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_fp8_forward_traced(const void* x, const float* router_logits, const uint8_t* w13,
+                           const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                           int T, int H, int I, int E, int top_k, int renormalize, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t events[MOE_STAGE_COUNT + 1]) {
+  if (!events) return MOE_ERR_NULL;
+  for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
+    if (!events[i]) return MOE_ERR_NULL;
+  return forward_impl(x, router_logits, w13, w13_scale, w2, w2_scale, T, H, I, E, top_k,
+                      renormalize, out, workspace, workspace_bytes, stream, events);
+}
+
+int per_token_group_quant_fp8(const void* x, int M, int K, int group_size, uint8_t* q,
+                              float* scales, hipStream_t stream) {
+  if (group_size != MOE_QUANT_GROUP) return MOE_ERR_UNSUPPORTED;
+  if (M < 0 || K < 128 || K % 128) return MOE_ERR_SHAPE;
+  if ((long long)M * K > (1LL << 40)) return MOE_ERR_SHAPE;
+  if (M == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_NULL;
+  if ((uintptr_t)x % 16 || (uintptr_t)q % 8 || (uintptr_t)scales % 4) return MOE_ERR_UNSUPPORTED;
+  const size_t n = (size_t)M * K;
+  if (overlaps(q, n, x, 2 * n) || overlaps(scales, n / 128 * 4, x, 2 * n) ||
+      overlaps(q, n, scales, n / 128 * 4))
+    return MOE_ERR_ALIAS;
+  return moe::launch_group_quant(x, M, K, q, scales, stream) ? MOE_ERR_HIP : MOE_OK;
+}
+
+int moe_topk_softmax(const float* logits, int T, int E, int top_k, int renormalize,
+                     int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || top_k < 1 || top_k > E || top_k > MOE_MAX_TOP_K)
+    return MOE_ERR_SHAPE;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  return moe::launch_topk_softmax(logits, T, E, top_k, renormalize, topk_ids, topk_weights, stream)
+             ? MOE_ERR_HIP
+             : MOE_OK;
+}
+
+size_t moe_align_scratch_bytes(int T, int top_k, int E) {
+  if (T < 0 || top_k < 1 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+  const long long P = (long long)T * top_k;
+  if (P > (long long)MOE_MAX_TOKENS * MOE_MAX_TOP_K) return 0;
+  return moe::align_scratch_bytes((int)P, E);
+}
+
+int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m, int32_t* sorted_ids,
+              int32_t* expert_ids, int32_t* num_tokens_post_padded, void* scratch,
+              size_t scratch_bytes, hipStream_t stream) {
+  if (T < 0 || top_k < 1 || E < 1 || E > MOE_MAX_EXPERTS || top_k > E) return MOE_ERR_SHAPE;
+  if ((long long)T * top_k > (long long)MOE_MAX_TOKENS * MOE_MAX_TOP_K) return MOE_ERR_SHAPE;
+  if (block_m < 16 || block_m > 256 || (block_m & (block_m - 1))) return MOE_ERR_SHAPE;
+  if (!sorted_ids || !expert_ids || !num_tokens_post_padded || !scratch) return MOE_ERR_NULL;
+  if (T > 0 && !topk_ids) return MOE_ERR_NULL;
+  const int P = T * top_k;
+  if (scratch_bytes < moe::align_scratch_bytes(P, E) || ((uintptr_t)scratch % 4))
+    return MOE_ERR_WORKSPACE;
+  return moe::launch_align(topk_ids, P, E, block_m, sorted_ids, expert_ids, num_tokens_post_padded,
+                           scratch, stream)
+             ? MOE_ERR_HIP
+             : MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+/*
+ * moe_fp8.h - C ABI of the MI355X (gfx950) fused FP8 block-quantized MoE
+ * layer forward and its stages.
+ *
+ * The operation is the fused MoE layer of the vLLM pages on quantization and
+ * MoE optimisations:
+ *   - overview page, "FusedMoE Class": experts w13 (gate+up) and w2 (down)
+ *     stored [num_experts, N, K], a top-K router in front;
+ *   - overview page, "Modular Kernel Architecture": quantize the inputs,
+ *     permute -> expert GEMMs -> unpermute, gather the results;
+ *   - overview page, "Triton Fused MoE Kernel": blocks of BLOCK_SIZE_M
+ *     sorted tokens that all belong to one expert; float32 dequantisation of
+ *     the quantized accumulation, then the router-weight multiply;
+ *   - fp8 oracle API page, make_fp8_moe_quant_config / quant keys: static
+ *     128x128 block weight scales (block_shape [128, 128]) and dynamic
+ *     per-token 128-group activation scales, symmetric, so no activation
+ *     scale is an input.
+ * The activation between the GEMMs is SiLU(gate) * up, requantised per token
+ * and 128-group before the second GEMM; routing is softmax top-k with
+ * optional renormalisation.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *     contiguous.  bf16 tensors are passed as const void* (raw 16-bit
+ *     bfloat16 words).  FP8 tensors hold OCP e4m3fn codes, one byte each.
+ *   - Scales are float32 dequant multipliers: value = dec(code) * scale.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without synchronising.  The library allocates no device memory
+ *     and keeps no mutable global state; calls on different streams with
+ *     disjoint outputs and workspaces may run concurrently.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     negative moe_status is returned on error and nothing is enqueued.  A
+ *     launch failure reported by the HIP runtime returns MOE_ERR_HIP.  On any
+ *     error the contents of the outputs are unspecified.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* a size is out of range or not a multiple of 128 */
+  MOE_ERR_UNSUPPORTED = -3, /* a valid request this library does not serve */
+  MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_fp8_workspace_bytes() */
+  MOE_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
+  MOE_ERR_ALIAS = -6        /* an output overlaps an input or the workspace */
+} moe_status;
+
+/* Limits.  H and I must be multiples of 128 (the weight block and activation
+ * group), 1 <= top_k <= E <= MOE_MAX_EXPERTS, 1 <= T <= MOE_MAX_TOKENS (the
+ * fused-MoE activation chunk of the overview page's environment-variable
+ * table is 16384 tokens; one call covers one such chunk). */
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_TOKENS 16384
+#define MOE_MAX_TOP_K 32
+#define MOE_QUANT_GROUP 128
+
+/* Intermediate tensors inside the forward's workspace, for inspection by
+ * tests (offsets from moe_fp8_workspace_layout, in bytes). */
+enum {
+  MOE_TAP_TOPK_IDS = 0,     /* int32 [T, top_k] expert id per slot, descending score */
+  MOE_TAP_TOPK_WEIGHTS,     /* float32 [T, top_k] routing weight per slot */
+  MOE_TAP_SORTED_IDS,       /* int32 [cap] pair index p = t*top_k + j, sentinel T*top_k */
+  MOE_TAP_EXPERT_IDS,       /* int32 [cap / block_m] expert of each block */
+  MOE_TAP_NTPP,             /* int32 [1] number of sorted rows after padding */
+  MOE_TAP_XQ,               /* uint8 [T, H] e4m3fn codes of x */
+  MOE_TAP_XS,               /* float32 [T, H/128] scales of x */
+  MOE_TAP_AQ,               /* uint8 [cap, I] requantised activation, sorted order */
+  MOE_TAP_AS,               /* float32 [cap, I/128] its scales */
+  MOE_TAP_Y,                /* bf16 [T*top_k, H] weighted expert output per pair */
+  MOE_TAP_ALIGN_SCRATCH,    /* int32 scratch of the sort-and-pad stage */
+  MOE_TAP_COUNT
+};
+
+/* Block size (BLOCK_SIZE_M: sorted rows per expert block) the forward uses
+ * for this shape.  Returns a positive power of two, or a negative moe_status
+ * for an invalid shape. */
+int moe_fp8_block_m(int T, int H, int I, int E, int top_k);
+
+/* Bytes of device workspace moe_fp8_forward needs for this shape (0 for an
+ * invalid shape).  The workspace must be 256-byte aligned. */
+size_t moe_fp8_workspace_bytes(int T, int H, int I, int E, int top_k);
+
+/* Byte offsets of the MOE_TAP_* tensors inside the workspace.  Writes
+ * MOE_TAP_COUNT entries into offsets (host memory).  Returns MOE_OK or a
+ * negative moe_status. */
+int moe_fp8_workspace_layout(int T, int H, int I, int E, int top_k,
+                             size_t offsets[MOE_TAP_COUNT]);
+
+/*
+ * Fused FP8 block-quantized MoE layer forward (FusedMoE.forward(hidden_states,
+ * router_logits) of the overview page, with the fp8 block-quant config):
+ *   (ids, w) = softmax top-k of router_logits (renormalised if asked)
+ *   (xq, xs) = per-token 128-group FP8 quantisation of x
+ *   h = block-scaled FP8 GEMM of xq with w13[e]        e = expert of the pair
+ *   a = silu(h[:, :I]) * h[:, I:], requantised per token and 128-group
+ *   y = block-scaled FP8 GEMM of a with w2[e], times the routing weight
+ *   out[t] = bf16( sum over the top_k slots of y )
+ *
+ *   x             bf16    [T, H]
+ *   router_logits float32 [T, E]
+ *   w13           e4m3fn  [E, 2I, H]      rows [0, I) gate, [I, 2I) up
+ *   w13_scale     float32 [E, 2I/128, H/128]
+ *   w2            e4m3fn  [E, H, I]
+ *   w2_scale      float32 [E, H/128, I/128]
+ *   renormalize   0 or 1
+ *   out           bf16    [T, H]; must not overlap any input or the workspace
+ *   workspace     device memory of at least moe_fp8_workspace_bytes(), 256-byte
+ *                 aligned, owned by the caller; its contents on return are the
+ *                 MOE_TAP_* intermediates (needs no initialisation)
+ */
+int moe_fp8_forward(const void* x, const float* router_logits,
+                    const uint8_t* w13, const float* w13_scale,
+                    const uint8_t* w2, const float* w2_scale,
+                    int T, int H, int I, int E, int top_k, int renormalize,
+                    void* out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Stages of the forward, in launch order (for moe_fp8_forward_traced). */
+enum {
+  MOE_STAGE_ROUTER = 0,     /* softmax top-k */
+  MOE_STAGE_ALIGN,          /* sort and pad by expert (three kernels) */
+  MOE_STAGE_QUANT,          /* activation quantisation of x */
+  MOE_STAGE_GEMM1,          /* w13 GEMM + SiLU*mul + requantisation */
+  MOE_STAGE_GEMM2,          /* w2 GEMM + routing weight */
+  MOE_STAGE_COMBINE,        /* weighted sum over the top_k slots */
+  MOE_STAGE_COUNT
+};
+
+/*
+ * moe_fp8_forward, plus tracing: records events[i] on `stream` just before
+ * stage i is enqueued and events[MOE_STAGE_COUNT] after the last one, so that
+ * hipEventElapsedTime(events[i], events[i+1]) is the GPU time of stage i.
+ * The MOE_STAGE_COUNT + 1 events are created by the caller (with timing
+ * enabled).  Same kernels and arguments as moe_fp8_forward.
+ */
+int moe_fp8_forward_traced(const void* x, const float* router_logits,
+                           const uint8_t* w13, const float* w13_scale,
+                           const uint8_t* w2, const float* w2_scale,
+                           int T, int H, int I, int E, int top_k, int renormalize,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, hipEvent_t events[MOE_STAGE_COUNT + 1]);
+
+/*
+ * Per-token-group dynamic FP8 activation quantisation (quant key
+ * kFp8Dynamic128Sym of the fp8 oracle API page; GROUP granularity of the
+ * overview page's "Weight Scale Granularities"):
+ *   s[m, g] = max(max_i |x[m, 128g + i]|, 1e-8) / 448     (float32, RNE)
+ *   q[m, k] = e4m3fn_RNE_saturate(x[m, k] / s[m, k / 128]) (float32 quotient)
+ *
+ *   x       bf16    [M, K]
+ *   q       e4m3fn  [M, K]
+ *   scales  float32 [M, K / group_size]
+ *   group_size must be 128; K must be a positive multiple of 128; M >= 0
+ *   (M == 0 enqueues nothing).
+ */
+int per_token_group_quant_fp8(const void* x, int M, int K, int group_size,
+                              uint8_t* q, float* scales, hipStream_t stream);
+
+/*
+ * Router stage alone (the top-K router of the overview page's "FusedMoE
+ * Class"): softmax over E logits, the top_k experts by logit (ties to the
+ * lower index) in descending order, weights renormalised to sum 1 if
+ * renormalize.  Same kernel as inside moe_fp8_forward.
+ *   logits float32 [T, E]; topk_ids int32 [T, top_k]; topk_weights float32 [T, top_k]
+ */
+int moe_topk_softmax(const float* logits, int T, int E, int top_k, int renormalize,
+                     int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/* Bytes of int32 scratch moe_align needs for P = T*top_k pairs and E experts. */
+size_t moe_align_scratch_bytes(int T, int top_k, int E);
+
+/*
+ * Sort-and-pad stage alone (the sorted-token blocks of the overview page's
+ * "Triton Fused MoE Kernel"): pairs p = t*top_k + j are grouped by expert in
+ * ascending p; each expert's run is padded with the sentinel T*top_k to a
+ * multiple of block_m; expert_ids[b] is the expert of rows
+ * [b*block_m, (b+1)*block_m); num_tokens_post_padded[0] is the padded total.
+ * Only the first num_tokens_post_padded rows are defined.  Same kernels as
+ * inside moe_fp8_forward.
+ *   topk_ids   int32 [T, top_k] values in [0, E) (pairs with other values are
+ *              left out of the layout)
+ *   sorted_ids int32 [T*top_k + E*(block_m-1)] (rounded up to block_m)
+ *   expert_ids int32 [that / block_m]
+ *   block_m    a power of two in [16, 256]
+ *   scratch    device memory of moe_align_scratch_bytes(), 256-byte aligned
+ */
+int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+              int32_t* sorted_ids, int32_t* expert_ids,
+              int32_t* num_tokens_post_padded,
+              void* scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* Static description of a moe_status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H */

@@ -1,0 +1,139 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/moe_fp8.h declares (and the binding knows them), and its host-side
+logic (argument checks, block size, workspace layout) behaves as documented.
+No kernel is launched: every call here fails validation before any HIP call,
+or is pure host arithmetic."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_block_quantized_amd as moe
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_fp8.h")
+
+
+def _declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True)
+    for name in _declared():
+        assert re.search(rf" T {name}$", nm.stdout, flags=re.M), name
+
+
+def test_status_strings():
+    lib = moe.load_library()
+    for code in range(-6, 1):
+        assert lib.moe_status_string(code)
+    assert lib.moe_status_string(7) == b"unknown status"
+
+
+@pytest.mark.parametrize("T,H,I,E,k,bad", [
+    (0, 256, 256, 8, 2, True), (16, 200, 256, 8, 2, True), (16, 256, 100, 8, 2, True),
+    (16, 256, 256, 0, 1, True), (16, 256, 256, 8, 9, True), (16, 256, 256, 513, 2, True),
+    (16385, 256, 256, 8, 2, True), (16, 256, 256, 64, 33, True), (16, 256, 256, 8, 0, True),
+    (16, 256, 256, 8, 2, False), (16384, 7168, 2048, 512, 32, False)])
+def test_shape_checks(T, H, I, E, k, bad):
+    ws = moe.moe_fp8_workspace_bytes(T, H, I, E, k)
+    bm = moe.load_library().moe_fp8_block_m(T, H, I, E, k)
+    if bad:
+        assert ws == 0 and bm == -2
+    else:
+        assert ws > 0 and bm in (16, 32, 64, 128)
+
+
+def test_block_m_choices():
+    bm = lambda *a: moe.moe_fp8_block_m(*a)
+    assert bm(64, 7168, 2048, 256, 8) == 16      # decode: ~2 pairs per expert
+    assert bm(1, 2048, 768, 128, 8) == 16
+    assert bm(64, 4096, 14336, 8, 2) == 32       # 16 pairs per expert
+    assert bm(8192, 7168, 2048, 256, 8) == 128   # prefill
+    assert bm(4096, 2048, 768, 128, 8) == 128
+
+
+def test_workspace_layout_is_disjoint_and_aligned():
+    for shape in [(16, 256, 512, 8, 2), (64, 7168, 2048, 256, 8), (8192, 7168, 2048, 256, 8),
+                  (1, 2048, 768, 128, 8), (512, 4096, 14336, 8, 2)]:
+        T, H, I, E, k = shape
+        off = moe.moe_fp8_workspace_layout(*shape)
+        total = moe.moe_fp8_workspace_bytes(*shape)
+        bm = moe.moe_fp8_block_m(*shape)
+        P = T * k
+        cap = -(-(P + E * (bm - 1)) // bm) * bm
+        size = {"topk_ids": 4 * P, "topk_weights": 4 * P, "sorted_ids": 4 * cap,
+                "expert_ids": 4 * (cap // bm), "ntpp": 4, "xq": T * H, "xs": 4 * T * H // 128,
+                "aq": cap * I, "as": 4 * cap * I // 128, "y": 2 * P * H, "align_scratch": 0}
+        names = moe.TAPS
+        for a, b in zip(names, names[1:]):
+            assert off[a] % 256 == 0
+            assert off[a] + size[a] <= off[b]
+        assert off[names[-1]] < total
+
+
+def test_forward_argument_checks():
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    fake = [vp(0x10000 * (i + 1)) for i in range(8)]   # never dereferenced: checks fail first
+    T, H, I, E, k = 16, 256, 512, 8, 2
+    need = moe.moe_fp8_workspace_bytes(T, H, I, E, k)
+    ws = vp(0x7000000000)
+
+    def call(args):
+        return lib.moe_fp8_forward(*args)
+
+    base = [fake[0], fake[1], fake[2], fake[3], fake[4], fake[5], T, H, I, E, k, 1,
+            vp(0x6000000000), ws, need, None]
+    for i in range(6):
+        a = list(base)
+        a[i] = None
+        assert call(a) == -1
+    a = list(base); a[12] = None; assert call(a) == -1
+    a = list(base); a[13] = None; assert call(a) == -1
+    a = list(base); a[7] = 300; assert call(a) == -2
+    a = list(base); a[11] = 2; assert call(a) == -2
+    a = list(base); a[14] = need - 1; assert call(a) == -4
+    a = list(base); a[13] = vp(0x7000000010); assert call(a) == -4          # misaligned
+    a = list(base); a[12] = vp(0x7000000000 + 512); assert call(a) == -6    # out inside workspace
+    a = list(base); a[12] = vp(fake[0].value + 256); assert call(a) == -6   # out overlaps x
+    a = list(base); a[0] = vp(fake[0].value + 2); assert call(a) == -3      # x not 16-byte aligned
+
+
+def test_stage_argument_checks():
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    assert lib.per_token_group_quant_fp8(vp(16), 4, 256, 64, vp(4096), vp(8192), None) == -3
+    assert lib.per_token_group_quant_fp8(vp(16), 4, 200, 128, vp(4096), vp(8192), None) == -2
+    assert lib.per_token_group_quant_fp8(vp(16), -1, 256, 128, vp(4096), vp(8192), None) == -2
+    assert lib.per_token_group_quant_fp8(None, 0, 256, 128, None, None, None) == 0   # empty: no-op
+    assert lib.per_token_group_quant_fp8(None, 4, 256, 128, vp(4096), vp(8192), None) == -1
+    assert lib.per_token_group_quant_fp8(vp(0x10000), 4, 256, 128, vp(0x10000 + 128), vp(1 << 30), None) == -6
+    assert lib.moe_topk_softmax(vp(16), 4, 8, 9, 1, vp(64), vp(128), None) == -2
+    assert lib.moe_topk_softmax(vp(16), 4, 600, 2, 1, vp(64), vp(128), None) == -2
+    assert lib.moe_topk_softmax(None, 4, 8, 2, 1, vp(64), vp(128), None) == -1
+    assert lib.moe_topk_softmax(None, 0, 8, 2, 1, None, None, None) == 0
+    n = lib.moe_align_scratch_bytes(64, 8, 256)
+    assert n == 2 * 1 * 256 * 4
+    assert lib.moe_align(vp(16), 64, 8, 256, 24, vp(64), vp(128), vp(256), vp(512), n, None) == -2
+    assert lib.moe_align(vp(16), 64, 8, 256, 16, vp(64), vp(128), vp(256), vp(512), n - 4, None) == -4
+    assert lib.moe_align(None, 64, 8, 256, 16, vp(64), vp(128), vp(256), vp(512), n, None) == -1
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        moe.per_token_group_quant_fp8(torch.zeros((2, 128), dtype=torch.bfloat16),
+                                      q=torch.zeros(1), scales=torch.zeros(1))
