@@ -23,14 +23,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// Correctly rounded float32 quotient x / s given r = RN(1 / s), from one
-// product and two fused multiply-adds (Markstein's correction step: with r
-// the correctly rounded reciprocal and q0 within an ulp of x / s, the
-// remainder x - q0*s is exact and q0 + rem*r rounds to RN(x / s)).
+// Correctly rounded float32 quotient x / s (s > 0) given r = RN(1 / s), from
+// one product and two fused multiply-adds (Markstein's correction step: with
+// r the correctly rounded reciprocal and q0 within an ulp of x / s, the
+// remainder x - q0*s is exact and q0 + rem*r rounds to RN(x / s)).  The
+// correction of an exact zero gives +0 whatever the sign of x, so the sign
+// is taken from x, as in the IEEE quotient.
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   float q0 = x * r;
   float rem = __builtin_fmaf(-q0, s, x);
-  return __builtin_fmaf(rem, r, q0);
+  return __builtin_copysignf(__builtin_fmaf(rem, r, q0), x);
 }
 
 __device__ __forceinline__ float clamp_fp8(float v) {

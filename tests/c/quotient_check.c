@@ -1,12 +1,15 @@
 /* Checks, on the host, the quotient the quantisation kernels compute:
- * q = fma(fma(-x*r, s, x), r, x*r) with s = max(amax, 1e-8)/448 and
- * r = 1/s (both IEEE float32 divisions), against the IEEE quotient x/s.
- *   mode "bf16": every positive bf16 amax and every bf16 x with 0 < x <= amax
- *                (the whole domain of the activation quantiser);
+ * q = copysign(fma(fma(-x*r, s, x), r, x*r), x) with s = max(amax, 1e-8)/448
+ * and r = 1/s (both IEEE float32 divisions), against the IEEE quotient x/s.
+ *   mode "bf16": every positive bf16 amax and every bf16 x with 0 <= x <= amax
+ *                (the whole domain of the activation quantiser, up to the
+ *                sign symmetry of IEEE rounding), plus -x for every fourth
+ *                amax and -0 for all;
  *   mode "random": N random float32 pairs with |x| <= amax (the
  *                requantisation domain).
- * Quotients below 2^-12 are skipped: every such value rounds to an e4m3 zero,
- * whose sign both forms keep.  Prints "checked mismatches". */
+ * The sign must agree on every quotient.  Below 2^-12 in magnitude only the
+ * sign is compared, since every such value rounds to an e4m3 zero of that
+ * sign.  Prints "checked mismatches". */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -20,11 +23,11 @@ static int check(float x, float amax, unsigned long long* n) {
   volatile float s = fmaxf(amax, 1e-8f) / 448.0f;
   volatile float r = 1.0f / s;
   volatile float ref = x / s;
-  if (fabsf(ref) < 0x1p-12f) return 0;
   volatile float q0 = x * r;
   volatile float rem = fmaf(-q0, s, x);
-  volatile float q = fmaf(rem, r, q0);
+  volatile float q = copysignf(fmaf(rem, r, q0), x);
   ++*n;
+  if (fabsf(ref) < 0x1p-12f) return (u_of(q) >> 31) != (u_of(ref) >> 31);
   return u_of(q) != u_of(ref);
 }
 
@@ -45,7 +48,10 @@ int main(int argc, char** argv) {
   } else {
     for (uint32_t a = 1; a < 0x7F80; ++a) {
       const float amax = f_of(a << 16);
-      for (uint32_t b = 1; b <= a; ++b) bad += check(f_of(b << 16), amax, &n);
+      for (uint32_t b = 0; b <= a; ++b) {
+        bad += check(f_of(b << 16), amax, &n);
+        if ((a & 3) == 0 || b == 0) bad += check(f_of((b << 16) | 0x80000000u), amax, &n);
+      }
     }
   }
   printf("%llu %llu\n", n, bad);

@@ -4,8 +4,16 @@ against the oracle.
 Exact targets, read from the documented workspace taps: routing ids, the
 sort-and-pad layout and the activation codes and scales.  The routing
 weights match within 1e-5 relative.  The requantised activation is not an
-exact target (its codes depend on the float32 accumulation order); the
-fraction of differing codes is reported and bounded.  The bf16 output must
+exact target: its codes depend on how the first GEMM accumulates.  The FP8
+MFMA sums the 128 products of one instruction with less than float32
+precision (measured on gfx950: up to ~8e-5 of sum |p| for operands spread
+over the whole e4m3 range, ~5e-6 for moderate ranges), so a few codes next
+to a rounding midpoint land on the neighbouring grid point.  The test
+requires fewer than 1% (+3) differing codes, each within one grid step of the
+oracle's plus 1/8 in units of the group scale (1/3584 of the group maximum:
+near zero the grid is finer than the MFMA error, which scales with the sum
+of |products| rather than with the result), and requant scales within 1e-3
+relative.  The bf16 output must
 satisfy |gpu - ref| <= 1e-2 + 2e-2 |ref| everywhere and a relative norm
 error below 1e-2: the expected difference is a few 1e-3, from the
 float32 accumulation order, the rare requant code flips it causes and the
@@ -22,6 +30,7 @@ import torch
 
 import fp8_block_quantized_amd as moe
 from oracle import align as ref_align
+from oracle import e4m3
 from oracle import moe as ref_moe
 from synth import make_activations, make_weights, moe_workload
 from tests.gpu_util import WEIGHT_RTOL, align_prefix, assert_out_close, note, np_, to_dev
@@ -48,11 +57,20 @@ def _check_taps(taps, info, ids_np, E, what):
 
 
 def _requant_mismatch(taps, info, sorted_rows, P, I):
-    """fraction of requantised codes that differ (sorted order -> pair order)"""
-    aq = np_(taps["aq"])
+    """fraction of requantised codes that differ (sorted order -> pair order);
+    asserts every difference is within one grid step + 1/8 and the scales
+    agree to 1e-3"""
+    aq, as_ = np_(taps["aq"]), np_(taps["as"])
     real = sorted_rows < P
     g = np.zeros((P, I), np.uint8)
     g[sorted_rows[real]] = aq[: sorted_rows.size][real]
+    gs = np.zeros((P, I // 128), np.float32)
+    gs[sorted_rows[real]] = as_[: sorted_rows.size][real]
+    np.testing.assert_allclose(gs, info["as"], rtol=1e-3, atol=0)
+    dg, dr = e4m3.decode(g), e4m3.decode(info["aq"])
+    allowed = 2 * e4m3.half_ulp(np.maximum(np.abs(dg), np.abs(dr))) + 0.125
+    worst = np.max(np.abs(dg - dr) - allowed)
+    assert worst <= 0, f"a requantised code is {worst} beyond one grid step + 1/8"
     return float(np.mean(g != info["aq"]))
 
 
@@ -68,7 +86,7 @@ def _full_case(w, renorm=True, what=""):
     assert np.array_equal(np_(taps["xq"]), info["xq"]), f"{what}: xq"
     assert np.array_equal(np_(taps["xs"]).view(np.uint32), info["xs"].view(np.uint32)), f"{what}: xs"
     mm = _requant_mismatch(taps, info, rows, T * k, I)
-    assert mm < 2e-3, f"{what}: requant code mismatch fraction {mm}"
+    assert mm * T * k * I <= 1e-2 * T * k * I + 3, f"{what}: requant code mismatch fraction {mm}"
     m = assert_out_close(np_(out.float()), ref, what)
     note(f"  max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e} requant_mismatch={mm:.2e}")
     return out

@@ -25,4 +25,4 @@ def test_quotient_is_ieee_division(exe, mode):
     args = [exe, mode] + (["20000000"] if mode == "random" else [])
     r = subprocess.run(args, capture_output=True, text=True, timeout=300)
     checked, bad = map(int, r.stdout.split())
-    assert checked > 10_000_000 and bad == 0
+    assert checked > 10_000_000 and bad == 0, (checked, bad)
