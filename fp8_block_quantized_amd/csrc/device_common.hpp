@@ -12,6 +12,8 @@ constexpr float kAmaxEps = 1e-8f;    // lower clamp of a group amax
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -52,6 +54,14 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 __device__ __forceinline__ void group_scale(float amax, float& s, float& r) {
   s = __builtin_fmaxf(amax, kAmaxEps) / kFp8Max;
   r = 1.0f / s;
+}
+
+// Four e4m3fn codes (one dword) -> four f16 values, exactly (every e4m3fn
+// value is an f16 value; the hardware conversion scales by 1.0).
+__device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, _Float16* out) {
+  const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int first_mask, int last_mask) {

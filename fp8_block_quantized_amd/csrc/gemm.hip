@@ -289,6 +289,218 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
   }
 }
 
+// GEMM1 with partial sums exact to about 1e-9 of their size.
+//
+// The requantisation after SiLU*mul is a step function: a code that moves
+// to the neighbouring e4m3 grid point shifts the whole output row by about
+// |w2| * (one grid step), so the intermediate a must round to the same
+// float32 as the exact product would.  The FP8 MFMA sums its products
+// below float32 precision (about 1.4e-6 of sum |p| per 128 products on
+// gfx950), which moves ~0.5% of those codes; so this GEMM converts both e4m3
+// operands exactly to f16 (v_cvt_scalef32_pk_f16_fp8 with scale 1) and runs
+// v_mfma_f32_16x16x32_f16 (four per 128-wide K block, chained), whose float32
+// accumulation of the exact 8-bit products is accurate to ~1e-10 of sum |p|.
+// Each block partial is scaled by xs * ws in float64 (exact) and summed in
+// float64, and SiLU*mul is evaluated in float64 before the one rounding of
+// a to float32.
+//
+// Workgroup = 4 waves, RM sorted rows x 256 weight rows (32 gate + 32 up per
+// wave); a block of BM rows is covered by BM / RM workgroups.  Token tiles
+// are staged in LDS already converted to f16 (RM x 128 x 2 bytes, XOR
+// swizzled on 16-byte chunks, double buffered); weight fragments stream
+// from HBM into registers one K block ahead and are converted there.
+template <int RM>
+__global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, int split) {
+  constexpr int NQ = RM / 16;
+  constexpr int CHUNKS = RM * 8;               // 16-byte fp8 chunks of a token tile
+  constexpr int CPT = (CHUNKS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][RM * 256];
+  __shared__ float red[4][RM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int L = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int per_b = split * args.n_tiles;
+  const int b = L / per_b;
+  const int rem = L - b * per_b;
+  const int half = rem / args.n_tiles, j = rem - half * args.n_tiles;
+  const int ntpp = *args.ntpp;
+  if (b * BM >= ntpp) return;
+  const int e = args.expert_ids[b];
+  const int K = args.K, nkb = K >> 7;
+  const int row0 = b * BM + half * RM;
+
+  int prow[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) prow[pp] = (pp < 2 ? 0 : args.I) + 128 * j + 32 * wave + 16 * (pp & 1);
+  const uint8_t* wbase = args.w + (size_t)e * args.N * K;
+  const uint8_t* wptr[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) wptr[pp] = wbase + (size_t)(prow[pp] + l16) * K + g * 16;
+  const int nblk_n = args.N >> 7;
+  const float* ws0 = args.w_scale + ((size_t)e * nblk_n + j) * nkb;
+  const float* ws1 = args.w_scale + ((size_t)e * nblk_n + (args.I >> 7) + j) * nkb;
+
+  const uint8_t* aptr[CPT];
+  int soff0[CPT], soff1[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
+    aptr[i] = nullptr;
+    soff0[i] = soff1[i] = -1;
+    if (c < CHUNKS) {
+      const int r = c >> 3, ch = c & 7;
+      soff0[i] = r * 256 + (((2 * ch) ^ (r & 15)) << 4);
+      soff1[i] = r * 256 + (((2 * ch + 1) ^ (r & 15)) << 4);
+      const int p = args.sorted_ids[row0 + r];
+      if (p < args.P) aptr[i] = args.act + (size_t)(p / args.top_k) * K + ch * 16;
+    }
+  }
+  const float* sptr[NQ];
+  int qoff[NQ][4];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int rq = 16 * q + l16;
+    const int p = args.sorted_ids[row0 + rq];
+    sptr[q] = p < args.P ? args.act_scale + (size_t)(p / args.top_k) * nkb : nullptr;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = 2 * g + (c & 1) + 8 * (c >> 1);
+      qoff[q][c] = rq * 256 + ((idx ^ (rq & 15)) << 4);
+    }
+  }
+
+  auto stage_tokens = [&](const uint4* regs, int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      if (soff0[i] < 0) continue;
+      _Float16 h[16];
+      e4m3x4_to_f16(regs[i].x, h);
+      e4m3x4_to_f16(regs[i].y, h + 4);
+      e4m3x4_to_f16(regs[i].z, h + 8);
+      e4m3x4_to_f16(regs[i].w, h + 12);
+      *(uint4*)(&smem[buf][soff0[i]]) = *(const uint4*)(h);
+      *(uint4*)(&smem[buf][soff1[i]]) = *(const uint4*)(h + 8);
+    }
+  };
+
+  uint4 areg[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) areg[i] = aptr[i] ? *(const uint4*)aptr[i] : make_uint4(0, 0, 0, 0);
+  v8i wcur[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) wcur[pp] = load_frag_global(wptr[pp]);
+  float sa[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) sa[q] = sptr[q] ? sptr[q][0] : 0.0f;
+  float sw0 = ws0[0], sw1 = ws1[0];
+  stage_tokens(areg, 0);
+  __syncthreads();
+
+  double acc[4][NQ][4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[pp][q][r] = 0.0;
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    const int kn = kb + 1 < nkb ? kb + 1 : kb;
+    const size_t koff = (size_t)kn * 128;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      areg[i] = aptr[i] ? *(const uint4*)(aptr[i] + koff) : make_uint4(0, 0, 0, 0);
+    v8i wnext[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) wnext[pp] = load_frag_global(wptr[pp] + koff);
+    float sa_n[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) sa_n[q] = sptr[q] ? sptr[q][kn] : 0.0f;
+    const float sw0_n = ws0[kn], sw1_n = ws1[kn];
+
+    v8h wf[4][4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        _Float16 h[8];
+        e4m3x4_to_f16((uint32_t)wcur[pp][2 * c], h);
+        e4m3x4_to_f16((uint32_t)wcur[pp][2 * c + 1], h + 4);
+        wf[pp][c] = *(const v8h*)h;
+      }
+    const double sw0d = (double)sw0, sw1d = (double)sw1;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      v8h tq[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) tq[c] = *(const v8h*)(&smem[buf][qoff[q][c]]);
+      const double sad = (double)sa[q];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][0], tq[0], zero, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][1], tq[1], part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][2], tq[2], part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][3], tq[3], part, 0, 0, 0);
+        const double sc = sad * (pp < 2 ? sw0d : sw1d);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fma((double)part[r], sc, acc[pp][q][r]);
+      }
+    }
+    if (kb + 1 < nkb) stage_tokens(areg, buf ^ 1);
+    __syncthreads();
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) wcur[pp] = wnext[pp];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) sa[q] = sa_n[q];
+    sw0 = sw0_n;
+    sw1 = sw1_n;
+  }
+
+  // a = silu(gate) * up in float64, rounded once to float32, then requantised
+  // per row over the 128 features of tile j
+  float av[NQ][2][4];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    float m = 0.0f;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double gt = acc[pg][q][r], up = acc[pg + 2][q][r];
+        const float a = (float)(gt / (1.0 + exp(-gt)) * up);
+        av[q][pg][r] = a;
+        m = __builtin_fmaxf(m, __builtin_fabsf(a));
+      }
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+    if (lane < 16) red[wave][16 * q + l16] = m;
+  }
+  __syncthreads();
+  const int Iq = args.I;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int rq = 16 * q + l16;
+    const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0][rq], red[1][rq]),
+                                       __builtin_fmaxf(red[2][rq], red[3][rq]));
+    float s, rcp;
+    group_scale(amax, s, rcp);
+    const size_t grow = (size_t)(row0 + rq);
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const int i = 128 * j + 32 * wave + 16 * pg + 4 * g;
+      const uint32_t word = pack4_e4m3(clamp_fp8(div_by_scale(av[q][pg][0], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][1], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][2], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][3], s, rcp)));
+      *(uint32_t*)(args.aq_out + grow * Iq + i) = word;
+    }
+    if (wave == 0 && lane < 16) args.as_out[grow * (Iq >> 7) + j] = s;
+  }
+}
+
 template <bool GEMM1>
 static hipError_t launch_gemm_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
@@ -312,7 +524,16 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
   a.aq_out = aq; a.as_out = as;
   a.K = H; a.N = 2 * I; a.I = I; a.H = H; a.P = P; a.top_k = top_k;
   a.n_tiles = I / 128; a.nblk = nblk;
-  return launch_gemm_bm<true>(a, BM, stream);
+  const int rm = BM < 32 ? BM : 32;
+  const int split = BM / rm;
+  const dim3 grid((unsigned)(nblk * split * a.n_tiles)), block(256);
+  if (rm == 16)
+    hipLaunchKernelGGL(moe_gemm1_kernel<16>, grid, block, 0, stream, a, BM, split);
+  else if (rm == 32)
+    hipLaunchKernelGGL(moe_gemm1_kernel<32>, grid, block, 0, stream, a, BM, split);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
