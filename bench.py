@@ -27,6 +27,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fused FP8 MoE tokens/s + % of HBM/MFMA roofline, decode M=64 & prefill M=8192"
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_FP8_PEAK = 5.0e15     # dense FP8 FLOP/s
+MFMA_F16_PEAK = 2.5e15     # dense f16 / bf16 FLOP/s
+# MFMA type of each contraction: GEMM1 runs on f16 MFMAs of exactly converted
+# e4m3 operands, GEMM2 on FP8 MFMAs
+STAGE_PEAK = {"gemm1": MFMA_F16_PEAK, "gemm2": MFMA_FP8_PEAK}
 
 
 def parse():
@@ -35,7 +39,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="dsv3", choices=["dsv3", "mixtral", "qwen3", "tiny"])
-    p.add_argument("--cpu-sample-tokens", type=int, default=4)
+    p.add_argument("--cpu-sample-tokens", type=int, default=12)
+    p.add_argument("--phase", default="both", choices=["both", "decode", "prefill"],
+                   help="time one batch size only (for per-kernel profiles)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args()
 
@@ -70,12 +76,12 @@ def algorithmic(ids, T, H, I, E, k):
     }
 
 
-def roofline_of(nbytes, flops, seconds):
-    t_hbm, t_mfma = nbytes / HBM_PEAK, flops / MFMA_FP8_PEAK
+def roofline_of(nbytes, flops, seconds, mfma_peak=MFMA_FP8_PEAK):
+    t_hbm, t_mfma = nbytes / HBM_PEAK, flops / mfma_peak
     if t_mfma > t_hbm:
         a = flops / seconds / 1e12
-        return {"bound": "mfma", "achieved": a, "peak": MFMA_FP8_PEAK / 1e12, "unit": "TFLOP/s",
-                "frac": a / (MFMA_FP8_PEAK / 1e12)}
+        return {"bound": "mfma", "achieved": a, "peak": mfma_peak / 1e12, "unit": "TFLOP/s",
+                "frac": a / (mfma_peak / 1e12)}
     a = nbytes / seconds / 1e9
     return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
             "frac": a / (HBM_PEAK / 1e9)}
@@ -132,11 +138,15 @@ def main():
     wts = {"w13": w13, "w13_scale": w13s, "w2": w2, "w2_scale": w2s}
     phases = {}
     for name, T in (("decode", T_dec), ("prefill", T_pre)):
+        if args.phase not in ("both", name):
+            continue
         x, logits = make_activations(H, E, T, base, c["logits"], dev)
         phases[name] = {"T": T, "x": x, "logits": logits,
                         "ws": moe.alloc_workspace(T, H, I, E, k, dev),
                         "out": torch.empty((T, H), dtype=torch.bfloat16, device=dev)}
     order = ["decode", "prefill"] if T_dec != T_pre else ["decode"]
+    if args.phase != "both":
+        order = [args.phase]
 
     def run(ph, events=None):
         moe.moe_fp8_forward(ph["x"], ph["logits"], w13, w13s, w2, w2s, k, True,
@@ -183,7 +193,8 @@ def main():
         }
         for s, v in zip(moe.STAGES, st_ms):
             b, f = alg["stage"][s]
-            kernels[f"{n}.{s}"] = {"ms": float(v), "bytes": b, "flops": f}
+            kernels[f"{n}.{s}"] = {"ms": float(v), "bytes": b, "flops": f,
+                                   "peak": STAGE_PEAK.get(s, MFMA_FP8_PEAK)}
 
     # standalone activation quantiser, rotating three input buffers (> MALL)
     from synth import QUANT_WORKLOAD
@@ -207,7 +218,7 @@ def main():
 
     dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
     dom = kernels[dom_name]
-    roof = roofline_of(dom["bytes"], dom["flops"], dom["ms"] * 1e-3)
+    roof = roofline_of(dom["bytes"], dom["flops"], dom["ms"] * 1e-3, dom["peak"])
     roof.update({"kernel": dom_name, "traffic": None,
                  "alg_bytes_per_launch": dom["bytes"], "alg_flops_per_launch": dom["flops"],
                  "ms_per_launch": dom["ms"]})
@@ -218,16 +229,17 @@ def main():
         "metric": METRIC, "value": tokens / (wall / args.steps), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8e4m3 x fp8e4m3 -> f32 accumulate (bf16 in/out)", "data": "synthetic",
+        "dtype": "fp8e4m3 (GEMM2 FP8 MFMA, f32 acc; GEMM1 exact f16 MFMA, f64 acc; bf16 in/out)",
+        "data": "synthetic",
         "config": {"workload": f"{args.workload}-shaped MoE layer H={H} I={I} E={E} top_k={k}, "
-                               f"decode T={T_dec} + prefill T={T_pre} per step",
-                   "H": H, "I": I, "E": E, "top_k": k, "T_decode": T_dec, "T_prefill": T_pre,
+                               + " + ".join(f"{n} T={phases[n]['T']}" for n in order) + " per step",
+                   "H": H, "I": I, "E": E, "top_k": k, "T": {n: phases[n]["T"] for n in order},
                    "block_m": {n: moe.moe_fp8_block_m(phases[n]["T"], H, I, E, k) for n in order}},
         "roofline": roof,
         "phases": result_phases,
         "quant_standalone": quant,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and "decode" in phases:
         ph = phases["decode"]
         out["cpu_baseline"] = cpu_baseline(wts, ph["x"], ph["logits"], k, args.cpu_sample_tokens)
     else:

@@ -13,23 +13,22 @@
 //   GEMM2: y[p, n] = w[p] * sum_kb as[r, kb] * w2s[e, n/128, kb]
 //                      * sum_{k in kb} dec(aq[r, k]) * dec(w2[e, n, k])
 //
-// Mapping onto gfx950.  One v_mfma_f32_16x16x128_f8f6f4 covers exactly one
-// 128-wide K block of a 16x16 output tile, so the product of a block is a
-// fresh MFMA result and its two scales are applied with one FMA per output
-// into the float32 accumulator: no partial sums span scale blocks.  Weights
-// sit on the MFMA's M side (16 weight rows per fragment) and tokens on its
-// N side: the decode-sized token counts still fill an MFMA, and every lane
-// ends up with four consecutive output features of one token, which the
-// epilogues store as packed words.
+// Common mapping onto gfx950.  A K step is one 128-wide scale block, so the
+// product of a block is a fresh MFMA result and its two scales are applied
+// once per output when it is folded into the accumulator: no partial sum
+// spans scale blocks.  Weights sit on the MFMA's M side (16 weight rows per
+// fragment) and tokens on its N side: decode-sized token counts still fill
+// an MFMA, and every lane ends up with four consecutive output features of
+// one token, which the epilogues store as packed words.  Each wave streams
+// its private weight rows from HBM straight into MFMA fragments one K block
+// ahead; the token tile of a K block is shared by the four waves of a
+// workgroup through an XOR-swizzled, double-buffered LDS tile.
 //
-// Workgroup = 4 waves, BM sorted rows x 256 weight rows.  Each wave owns 64
-// weight rows and streams them from HBM straight into MFMA fragments (no LDS
-// round trip: the rows are private to the wave), one K block ahead of the
-// MFMAs.  The BM x 128 token tile of each K block is shared by the four
-// waves through an XOR-swizzled, double-buffered LDS tile.  For GEMM1 a wave
-// owns 32 gate rows and the 32 up rows of the same features, so SiLU*mul is
-// elementwise in registers; the 128 features of a requant group span the
-// four waves, whose row maxima meet in LDS.
+// GEMM2 uses v_mfma_f32_16x16x128_f8f6f4 (one per 16x16 tile and K block)
+// with a float32 accumulator; workgroup = BM sorted rows x 256 output
+// features, 64 per wave.  GEMM1 needs partial sums far more exact than the
+// FP8 MFMA gives (see moe_gemm1_kernel) and runs on f16 MFMAs of exactly
+// converted operands with float64 accumulation.
 //
 // Work order: logical tile L = m_block * n_tiles + n_tile, and the XCD
 // renumbering gives every XCD a contiguous range of L, so tiles sharing a
@@ -73,17 +72,12 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
   return r;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
-
-template <int BM, bool GEMM1>
-__global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
+template <int BM>
+__global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   constexpr int NQ = BM / 16;                  // token sub-tiles
   constexpr int CHUNKS = BM * 8;               // 16-byte chunks of a token tile
   constexpr int CPT = (CHUNKS + 255) / 256;    // chunks per thread
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][BM * 128];
-  __shared__ float red[4][BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -96,32 +90,18 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
   const int row0 = b * BM;
 
   // ---- weight side: 4 fragments of 16 rows per wave ----
-  bool wave_on = true;
+  // (the last tile of an H that is not a multiple of 256 has two idle waves)
+  const bool wave_on = 256 * j + 64 * wave < args.N;
   int prow[4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    if (GEMM1)
-      prow[pp] = (pp < 2 ? 0 : args.I) + 128 * j + 32 * wave + 16 * (pp & 1);
-    else
-      prow[pp] = 256 * j + 64 * wave + 16 * pp;
-  }
-  if (!GEMM1 && 256 * j + 64 * wave >= args.N) wave_on = false;
+  for (int pp = 0; pp < 4; ++pp) prow[pp] = 256 * j + 64 * wave + 16 * pp;
   const uint8_t* wbase = args.w + (size_t)e * args.N * K;
   const uint8_t* wptr[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp)
     wptr[pp] = wbase + (size_t)(wave_on ? prow[pp] + l16 : l16) * K + g * 16;
   const int nblk_n = args.N >> 7;
-  const float* ws0;
-  const float* ws1;
-  if (GEMM1) {
-    ws0 = args.w_scale + ((size_t)e * nblk_n + j) * nkb;                       // gate block
-    ws1 = args.w_scale + ((size_t)e * nblk_n + (args.I >> 7) + j) * nkb;       // up block
-  } else {
-    const int nb = wave_on ? (256 * j + 64 * wave) >> 7 : 0;
-    ws0 = args.w_scale + ((size_t)e * nblk_n + nb) * nkb;
-    ws1 = ws0;
-  }
+  const float* ws0 = args.w_scale + ((size_t)e * nblk_n + (wave_on ? (256 * j + 64 * wave) >> 7 : 0)) * nkb;
 
   // ---- token side: BM x 128 tile per K block, staged in LDS ----
   const uint8_t* aptr[CPT];
@@ -134,12 +114,7 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
     if (c < CHUNKS) {
       const int r = c >> 3, ch = c & 7;
       soff[i] = r * 128 + ((ch ^ (r & 7)) << 4);
-      if (GEMM1) {
-        const int p = args.sorted_ids[row0 + r];
-        if (p < args.P) aptr[i] = args.act + (size_t)(p / args.top_k) * K + ch * 16;
-      } else {
-        aptr[i] = args.act + (size_t)(row0 + r) * K + ch * 16;
-      }
+      aptr[i] = args.act + (size_t)(row0 + r) * K + ch * 16;
     }
   }
   const float* sptr[NQ];
@@ -147,12 +122,7 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int rq = 16 * q + l16;
-    if (GEMM1) {
-      const int p = args.sorted_ids[row0 + rq];
-      sptr[q] = p < args.P ? args.act_scale + (size_t)(p / args.top_k) * nkb : nullptr;
-    } else {
-      sptr[q] = args.act_scale + (size_t)(row0 + rq) * nkb;
-    }
+    sptr[q] = args.act_scale + (size_t)(row0 + rq) * nkb;
     qoff0[q] = rq * 128 + ((g ^ (rq & 7)) << 4);
     qoff1[q] = rq * 128 + (((g + 4) ^ (rq & 7)) << 4);
   }
@@ -166,8 +136,8 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
   for (int pp = 0; pp < 4; ++pp) wcur[pp] = load_frag_global(wptr[pp]);
   float sa[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) sa[q] = sptr[q] ? sptr[q][0] : 0.0f;
-  float sw0 = ws0[0], sw1 = ws1[0];
+  for (int q = 0; q < NQ; ++q) sa[q] = sptr[q][0];
+  float sw0 = ws0[0];
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
     if (soff[i] >= 0) *(uint4*)(&smem[0][soff[i]]) = areg[i];
@@ -193,8 +163,8 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
     for (int pp = 0; pp < 4; ++pp) wnext[pp] = load_frag_global(wptr[pp] + koff);
     float sa_n[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) sa_n[q] = sptr[q] ? sptr[q][kn] : 0.0f;
-    const float sw0_n = ws0[kn], sw1_n = ws1[kn];
+    for (int q = 0; q < NQ; ++q) sa_n[q] = sptr[q][kn];
+    const float sw0_n = ws0[kn];
 
     // MFMAs on K block kb
 #pragma unroll
@@ -204,13 +174,11 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
       v8i bq;
       bq[0] = t0.x; bq[1] = t0.y; bq[2] = t0.z; bq[3] = t0.w;
       bq[4] = t1.x; bq[5] = t1.y; bq[6] = t1.z; bq[7] = t1.w;
-      const float sc0 = sa[q] * sw0;
-      const float sc1 = sa[q] * sw1;
+      const float sc = sa[q] * sw0;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
         const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             wcur[pp], bq, zero, 0, 0, 0, 0, 0, 0);
-        const float sc = (GEMM1 && pp >= 2) ? sc1 : sc0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
       }
@@ -226,65 +194,24 @@ __global__ __launch_bounds__(256) void moe_gemm_kernel(GemmArgs args) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) sa[q] = sa_n[q];
     sw0 = sw0_n;
-    sw1 = sw1_n;
   }
 
-  if (GEMM1) {
-    // a = silu(gate) * up, requantised per row over the 128 features of tile j
-    float av[NQ][2][4];
+  // y[p] = routing weight * acc, bf16, in pair order (real rows only)
+  if (!wave_on) return;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      float m = 0.0f;
+  for (int q = 0; q < NQ; ++q) {
+    const int rq = 16 * q + l16;
+    const int p = args.sorted_ids[row0 + rq];
+    if (p >= args.P) continue;
+    const float wt = args.topk_w[p];
+    uint16_t* yrow = args.y_out + (size_t)p * args.H;
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = silu_mul(acc[pg][q][r], acc[pg + 2][q][r]);
-          av[q][pg][r] = a;
-          m = __builtin_fmaxf(m, __builtin_fabsf(a));
-        }
-      m = __builtin_fmaxf(m, __shfl_xor(m, 16));
-      m = __builtin_fmaxf(m, __shfl_xor(m, 32));
-      if (lane < 16) red[wave][16 * q + l16] = m;
-    }
-    __syncthreads();
-    const int Iq = args.I;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int rq = 16 * q + l16;
-      const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0][rq], red[1][rq]),
-                                         __builtin_fmaxf(red[2][rq], red[3][rq]));
-      float s, rcp;
-      group_scale(amax, s, rcp);
-      const size_t grow = (size_t)(row0 + rq);
-#pragma unroll
-      for (int pg = 0; pg < 2; ++pg) {
-        const int i = 128 * j + 32 * wave + 16 * pg + 4 * g;
-        const uint32_t word = pack4_e4m3(clamp_fp8(div_by_scale(av[q][pg][0], s, rcp)),
-                                         clamp_fp8(div_by_scale(av[q][pg][1], s, rcp)),
-                                         clamp_fp8(div_by_scale(av[q][pg][2], s, rcp)),
-                                         clamp_fp8(div_by_scale(av[q][pg][3], s, rcp)));
-        *(uint32_t*)(args.aq_out + grow * Iq + i) = word;
-      }
-      if (wave == 0 && lane < 16) args.as_out[grow * (Iq >> 7) + j] = s;
-    }
-  } else {
-    if (!wave_on) return;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int rq = 16 * q + l16;
-      const int p = args.sorted_ids[row0 + rq];
-      if (p >= args.P) continue;
-      const float wt = args.topk_w[p];
-      uint16_t* yrow = args.y_out + (size_t)p * args.H;
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int h0 = 256 * j + 64 * wave + 16 * pp + 4 * g;
-        uint2 v;
-        v.x = f32_to_bf16_bits(acc[pp][q][0] * wt) | (f32_to_bf16_bits(acc[pp][q][1] * wt) << 16);
-        v.y = f32_to_bf16_bits(acc[pp][q][2] * wt) | (f32_to_bf16_bits(acc[pp][q][3] * wt) << 16);
-        *(uint2*)(yrow + h0) = v;
-      }
+    for (int pp = 0; pp < 4; ++pp) {
+      const int h0 = 256 * j + 64 * wave + 16 * pp + 4 * g;
+      uint2 v;
+      v.x = f32_to_bf16_bits(acc[pp][q][0] * wt) | (f32_to_bf16_bits(acc[pp][q][1] * wt) << 16);
+      v.y = f32_to_bf16_bits(acc[pp][q][2] * wt) | (f32_to_bf16_bits(acc[pp][q][3] * wt) << 16);
+      *(uint2*)(yrow + h0) = v;
     }
   }
 }
@@ -501,14 +428,13 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
   }
 }
 
-template <bool GEMM1>
-static hipError_t launch_gemm_bm(const GemmArgs& a, int BM, hipStream_t stream) {
+static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
   switch (BM) {
-    case 16: hipLaunchKernelGGL((moe_gemm_kernel<16, GEMM1>), grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((moe_gemm_kernel<32, GEMM1>), grid, block, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((moe_gemm_kernel<64, GEMM1>), grid, block, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((moe_gemm_kernel<128, GEMM1>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(moe_gemm2_kernel<16>, grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL(moe_gemm2_kernel<32>, grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL(moe_gemm2_kernel<64>, grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(moe_gemm2_kernel<128>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -546,7 +472,7 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
   a.y_out = y;
   a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
   a.n_tiles = (H + 255) / 256; a.nblk = nblk;
-  return launch_gemm_bm<false>(a, BM, stream);
+  return launch_gemm2_bm(a, BM, stream);
 }
 
 }  // namespace moe
