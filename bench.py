@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--phase", default="both", choices=["both", "decode", "prefill"],
                    help="time one batch size only (for per-kernel profiles)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="also run a plain device-to-device copy of this many MiB (three times), "
+                        "the reference kernel that scales the HBM byte counters")
     return p.parse_args()
 
 
@@ -195,6 +198,16 @@ def main():
             b, f = alg["stage"][s]
             kernels[f"{n}.{s}"] = {"ms": float(v), "bytes": b, "flops": f,
                                    "peak": STAGE_PEAK.get(s, MFMA_FP8_PEAK)}
+
+    if args.copy_calibration_mib:
+        nb = args.copy_calibration_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # standalone activation quantiser, rotating three input buffers (> MALL)
     from synth import QUANT_WORKLOAD

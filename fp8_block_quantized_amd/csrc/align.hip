@@ -40,7 +40,7 @@ __global__ __launch_bounds__(1024) void align_count_kernel(const int32_t* __rest
 __global__ __launch_bounds__(1024) void align_scan_kernel(
     const int32_t* __restrict__ counts, int nchunk, int E, int BM, int P,
     int32_t* __restrict__ base, int32_t* __restrict__ sorted_ids,
-    int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp) {
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp, int32_t* __restrict__ eoff) {
   __shared__ int scan[kChunk];
   const int e = threadIdx.x;
   int total = 0;
@@ -59,6 +59,9 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
   const int excl = incl - pad;
   const int padded_total = scan[kChunk - 1];
   if (e == 0) ntpp[0] = padded_total;
+  // first block of every expert, and the number of blocks in use after them
+  if (e < E) eoff[e] = excl / BM;
+  if (e == 0) eoff[E] = padded_total / BM;
   if (e < E) {
     int run = excl;
     for (int b = 0; b < nchunk; ++b) {
@@ -108,9 +111,16 @@ __global__ __launch_bounds__(1024) void align_scatter_kernel(
   }
 }
 
+// scratch: per-chunk counts and bases [nchunk, E] each, then the expert
+// block offsets [E + 1] that the GEMMs use to order their tiles
 size_t align_scratch_bytes(int P, int E) {
   const size_t nchunk = ((size_t)P + kChunk - 1) / kChunk;
-  return 2 * nchunk * (size_t)E * sizeof(int32_t);
+  return (2 * nchunk * (size_t)E + (size_t)E + 1) * sizeof(int32_t);
+}
+
+const int32_t* align_expert_offsets(const void* scratch, int P, int E) {
+  const size_t nchunk = ((size_t)P + kChunk - 1) / kChunk;
+  return (const int32_t*)scratch + 2 * nchunk * (size_t)E;
 }
 
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
@@ -118,12 +128,13 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
   const int nchunk = (P + kChunk - 1) / kChunk;
   int32_t* counts = (int32_t*)scratch;
   int32_t* base = counts + (size_t)nchunk * E;
+  int32_t* eoff = base + (size_t)nchunk * E;
   int ebits = 0;
   while ((1 << ebits) < E) ++ebits;
   if (nchunk > 0)
     hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, P, E, counts);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kChunk), 0, stream, counts, nchunk, E, BM, P,
-                     base, sorted_ids, expert_ids, ntpp);
+                     base, sorted_ids, expert_ids, ntpp, eoff);
   if (nchunk > 0)
     hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, P, E, ebits,
                        base, sorted_ids);

@@ -42,6 +42,7 @@ namespace moe {
 
 struct GemmArgs {
   const uint8_t* act;        // GEMM1: xq [T, H]        GEMM2: aq [cap, I]
+  const void* act_h;         // GEMM1: f16 dec(xq) [T, H]
   const float* act_scale;    // GEMM1: xs [T, H/128]    GEMM2: as [cap, I/128]
   const uint8_t* w;          // GEMM1: w13 [E, 2I, H]   GEMM2: w2 [E, H, I]
   const float* w_scale;      // [E, N/128, K/128]
@@ -60,7 +61,63 @@ struct GemmArgs {
   int top_k;
   int n_tiles;               // I/128 (GEMM1) or ceil(H/256) (GEMM2)
   int nblk;                  // m blocks in the grid (row capacity / BM)
+  const int32_t* eoff;       // [E + 1] first block of each expert, blocks in use
+  int E;
+  int split;                 // workgroups per row block (BM / rows per workgroup)
 };
+
+// M0 is written only inside these statements, each right before its load;
+// the compiler uses M0 nowhere else in this file.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_raw() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// Tile order.  Workgroups are numbered expert by expert, then by weight
+// tile, then over the expert's row blocks (split into `split` workgroups
+// each), so the workgroups that read one expert's weight panel run at the same
+// time and, with the XCD renumbering over the tiles in use, on one XCD: the
+// panel comes from HBM once and from L2 for the other row blocks, and the
+// token tiles they read meet in L2 and the MALL across weight tiles.  The
+// grid is sized from the row capacity; workgroups past the tiles in use leave.
+struct TileCoord {
+  int b, half, j;
+  bool valid;
+};
+
+__device__ __forceinline__ TileCoord tile_of(int bid, const GemmArgs& a) {
+  const int per_block = a.split * a.n_tiles;
+  const int n_real = load_uniform(a.eoff + a.E) * per_block;
+  if (bid >= n_real) return {0, 0, 0, false};
+  const int L = xcd_contiguous_id(bid, n_real);
+  int lo = 0, hi = a.E - 1;           // the last expert whose first tile is <= L
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (load_uniform(a.eoff + mid) * per_block <= L) lo = mid; else hi = mid - 1;
+  }
+  const int b0 = load_uniform(a.eoff + lo), nsub = (load_uniform(a.eoff + lo + 1) - b0) * a.split;
+  const int local = L - b0 * per_block;
+  const int j = local / nsub, sub = local - j * nsub;
+  return {b0 + sub / a.split, sub % a.split, j, true};
+}
+
 
 __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
   // 32 bytes of one row: K chunk g and chunk g+4 of the 128-byte block
@@ -81,11 +138,10 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int L = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  const int b = L / args.n_tiles, j = L - b * args.n_tiles;
-  const int ntpp = *args.ntpp;
-  if (b * BM >= ntpp) return;
-  const int e = args.expert_ids[b];
+  const TileCoord tc = tile_of(blockIdx.x, args);
+  if (!tc.valid) return;
+  const int b = tc.b, j = tc.j;
+  const int e = load_uniform(args.expert_ids + b);
   const int K = args.K, nkb = K >> 7;
   const int row0 = b * BM;
 
@@ -246,16 +302,13 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const int L = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  const int per_b = split * args.n_tiles;
-  const int b = L / per_b;
-  const int rem = L - b * per_b;
-  const int half = rem / args.n_tiles, j = rem - half * args.n_tiles;
-  const int ntpp = *args.ntpp;
-  if (b * BM >= ntpp) return;
-  const int e = args.expert_ids[b];
-  const int K = args.K, nkb = K >> 7;
+  const TileCoord tc = tile_of(blockIdx.x, args);
+  if (!tc.valid) return;
+  const int b = tc.b, half = tc.half, j = tc.j;
   const int row0 = b * BM + half * RM;
+  if (split > 1 && load_uniform(args.sorted_ids + row0) >= args.P) return;   // padding only
+  const int e = load_uniform(args.expert_ids + b);
+  const int K = args.K, nkb = K >> 7;
 
   int prow[4];
 #pragma unroll
@@ -428,8 +481,305 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill kernels: a three-stage LDS ring filled by direct global->LDS loads.
+//
+// With 128-row blocks the GEMMs are compute- and L2-bandwidth-heavy, and a
+// one-block register prefetch cannot cover the load latency.  These kernels
+// keep two K blocks of weights and tokens in flight through LDS
+// (global_load_lds_dwordx4 writes each lane's 16 bytes straight into LDS, no
+// registers involved; the XOR swizzle is produced by permuting the source
+// addresses).  The loads and their waits are inline asm: the compiler would
+// otherwise wait for every outstanding LDS load before each LDS read, since
+// it cannot tell the ring's stages apart, which serialises the pipeline.
+// Per K block: wait until the oldest stage has landed (vmcnt), barrier, issue
+// the stage two blocks ahead into the slot every wave finished reading one
+// iteration ago, compute.  Everything the loop reads besides the ring comes
+// through scalar loads, so no compiler-inserted vector-memory wait drains the
+// ring.
+// ---------------------------------------------------------------------------
+constexpr int kRingStages = 3;
+constexpr int kRingW = 256 * 128;      // 256 weight rows x one 128-byte K block
+constexpr int kRingS = 1024;           // token scales (four 256-byte wave slots)
+constexpr int kLoadsPerStage = 13;     // DMA instructions per wave per stage
+
+// GEMM2 prefill: 128 sorted rows x 256 output features per workgroup; wave w
+// owns features [64w, 64w+64) (4 MFMA rows) against all 8 token sub-tiles.
+__global__ __launch_bounds__(256) void moe_gemm2_pf_kernel(GemmArgs args) {
+  constexpr int BM = 128;
+  constexpr int kA = BM * 128, kStage = kRingW + kA + kRingS;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingStages * kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const TileCoord tc = tile_of(blockIdx.x, args);
+  if (!tc.valid) return;
+  const int b = tc.b, j = tc.j;
+  const int e = load_uniform(args.expert_ids + b);
+  const int K = args.K, nkb = K >> 7;
+  const int row0 = b * BM, n0 = 256 * j;
+
+  const uint8_t* wsrc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pos = (wave * 8 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+    const int row = n0 + r < args.N ? n0 + r : 0;    // rows past H: any valid row, never stored
+    wsrc[i] = args.w + ((size_t)e * args.N + row) * K + lc * 16;
+  }
+  const uint8_t* asrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+    asrc[i] = args.act + (size_t)(row0 + r) * K + lc * 16;
+  }
+  const float* ssrc = args.act_scale + (size_t)(row0 + (wave & 1) * 64 + lane) * nkb;
+  auto issue = [&](int stage, int kb) {
+    const uint32_t base = lds_offset(ring + stage * kStage);
+    const size_t ko = (size_t)kb * 128;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(wsrc[i] + ko, base + (wave * 8 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(asrc[i] + ko, base + kRingW + (wave * 4 + i) * 1024);
+    dma4(ssrc + kb, base + kRingW + kA + wave * 256);
+  };
+  const float* wsp = args.w_scale +
+      ((size_t)e * (args.N >> 7) + ((n0 + 64 * wave < args.N ? n0 + 64 * wave : 0) >> 7)) * nkb;
+  int poff[4][2], qoff[8][2];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int r = 64 * wave + 16 * pp + l16;
+    poff[pp][0] = r * 128 + ((g ^ (r & 7)) << 4);
+    poff[pp][1] = r * 128 + (((g + 4) ^ (r & 7)) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = 16 * q + l16;
+    qoff[q][0] = kRingW + r * 128 + ((g ^ (r & 7)) << 4);
+    qoff[q][1] = kRingW + r * 128 + (((g + 4) ^ (r & 7)) << 4);
+  }
+  v4f acc[4][8];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) wait_vmem<kLoadsPerStage>(); else wait_vmem<0>();
+    barrier_raw();
+    if (kb + 2 < nkb) issue((kb + 2) % kRingStages, kb + 2);
+    const uint8_t* st = ring + (kb % kRingStages) * kStage;
+    const float sw = load_uniform(wsp + kb);
+    v8i pf[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const uint4 a0 = *(const uint4*)(st + poff[pp][0]);
+      const uint4 a1 = *(const uint4*)(st + poff[pp][1]);
+      pf[pp] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 b0 = *(const uint4*)(st + qoff[q][0]);
+      const uint4 b1 = *(const uint4*)(st + qoff[q][1]);
+      const v8i bq = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      const float sc = *(const float*)(st + kRingW + kA + (16 * q + l16) * 4) * sw;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf[pp], bq, zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
+      }
+    }
+  }
+  // y[p] = routing weight * acc, bf16, in pair order (real rows only)
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int p = args.sorted_ids[row0 + 16 * q + l16];
+    if (p >= args.P) continue;
+    const float wt = args.topk_w[p];
+    uint16_t* yrow = args.y_out + (size_t)p * args.H;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const int h0 = n0 + 64 * wave + 16 * pp + 4 * g;
+      if (h0 >= args.H) continue;
+      uint2 v;
+      v.x = f32_to_bf16_bits(acc[pp][q][0] * wt) | (f32_to_bf16_bits(acc[pp][q][1] * wt) << 16);
+      v.y = f32_to_bf16_bits(acc[pp][q][2] * wt) | (f32_to_bf16_bits(acc[pp][q][3] * wt) << 16);
+      *(uint2*)(yrow + h0) = v;
+    }
+  }
+}
+
+// GEMM1 prefill, with the exact partial sums of moe_gemm1_kernel: a 128-row
+// block is covered by two workgroups of 64 rows (a half that holds only
+// padding leaves at once); each workgroup takes 256 weight rows, the gate and
+// up rows of 128 features.  Weights stay e4m3 in the ring and are converted
+// to f16 after the LDS read; tokens arrive already as f16 (dec(xq), written
+// by the activation quantiser).  Wave w owns gate rows [32w, 32w+32) and the
+// matching up rows against all four token sub-tiles.
+__global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
+  constexpr int BM = 128, RM = 64;
+  constexpr int kA = RM * 256, kStage = kRingW + kA + kRingS;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingStages * kStage];
+  __shared__ float red[4][RM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const TileCoord tc = tile_of(blockIdx.x, args);
+  if (!tc.valid) return;
+  const int b = tc.b, half = tc.half, j = tc.j;
+  const int row0 = b * BM + half * RM;
+  if (load_uniform(args.sorted_ids + row0) >= args.P) return;   // padding-only half
+  const int e = load_uniform(args.expert_ids + b);
+  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * j;
+
+  const uint8_t* wsrc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pos = (wave * 8 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+    const int wrow = r < 128 ? i0 + r : I + i0 + (r - 128);
+    wsrc[i] = args.w + ((size_t)e * args.N + wrow) * K + lc * 16;
+  }
+  const uint8_t* xh = (const uint8_t*)args.act_h;
+  const uint8_t* asrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 4, lc = (pos & 15) ^ (r & 15);
+    const int p = args.sorted_ids[row0 + r];
+    const int t = p < args.P ? p / args.top_k : 0;   // padding rows: any valid row
+    asrc[i] = xh + (size_t)t * K * 2 + lc * 16;
+  }
+  const float* ssrc;
+  {
+    const int p = args.sorted_ids[row0 + lane];
+    ssrc = args.act_scale + (size_t)(p < args.P ? p / args.top_k : 0) * nkb;
+  }
+  auto issue = [&](int stage, int kb) {
+    const uint32_t base = lds_offset(ring + stage * kStage);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(wsrc[i] + (size_t)kb * 128, base + (wave * 8 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(asrc[i] + (size_t)kb * 256, base + kRingW + (wave * 4 + i) * 1024);
+    dma4(ssrc + kb, base + kRingW + kA + wave * 256);
+  };
+  const int nbn = args.N >> 7;
+  const float* wsg = args.w_scale + ((size_t)e * nbn + j) * nkb;
+  const float* wsu = args.w_scale + ((size_t)e * nbn + (I >> 7) + j) * nkb;
+  int poff[4][2], qoff[4][4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int r = (pp < 2 ? 32 * wave + 16 * pp : 128 + 32 * wave + 16 * (pp - 2)) + l16;
+    poff[pp][0] = r * 128 + ((g ^ (r & 7)) << 4);
+    poff[pp][1] = r * 128 + (((g + 4) ^ (r & 7)) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * q + l16;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = 2 * g + (c & 1) + 8 * (c >> 1);
+      qoff[q][c] = kRingW + r * 256 + ((idx ^ (r & 15)) << 4);
+    }
+  }
+  double acc[4][4][4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[pp][q][r] = 0.0;
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) wait_vmem<kLoadsPerStage>(); else wait_vmem<0>();
+    barrier_raw();
+    if (kb + 2 < nkb) issue((kb + 2) % kRingStages, kb + 2);
+    const uint8_t* st = ring + (kb % kRingStages) * kStage;
+    const double swg = (double)load_uniform(wsg + kb), swu = (double)load_uniform(wsu + kb);
+    v8h wf[4][4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const uint4 a0 = *(const uint4*)(st + poff[pp][0]);
+      const uint4 a1 = *(const uint4*)(st + poff[pp][1]);
+      const uint32_t wd[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        _Float16 h[8];
+        e4m3x4_to_f16(wd[2 * c], h);
+        e4m3x4_to_f16(wd[2 * c + 1], h + 4);
+        wf[pp][c] = *(const v8h*)h;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v8h tq[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) tq[c] = *(const v8h*)(st + qoff[q][c]);
+      const double sad = (double)*(const float*)(st + kRingW + kA + (16 * q + l16) * 4);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][0], tq[0], zero, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][1], tq[1], part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][2], tq[2], part, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][3], tq[3], part, 0, 0, 0);
+        const double sc = sad * (pp < 2 ? swg : swu);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fma((double)part[r], sc, acc[pp][q][r]);
+      }
+    }
+  }
+
+  // a = silu(gate) * up in float64, rounded once to float32, requantised per
+  // row over the 128 features of tile j
+  float av[4][2][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float m = 0.0f;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double gt = acc[pg][q][r], up = acc[pg + 2][q][r];
+        const float a = (float)(gt / (1.0 + exp(-gt)) * up);
+        av[q][pg][r] = a;
+        m = __builtin_fmaxf(m, __builtin_fabsf(a));
+      }
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+    if (lane < 16) red[wave][16 * q + l16] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rq = 16 * q + l16;
+    const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0][rq], red[1][rq]),
+                                       __builtin_fmaxf(red[2][rq], red[3][rq]));
+    float s, rcp;
+    group_scale(amax, s, rcp);
+    const size_t grow = (size_t)(row0 + rq);
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const int i = i0 + 32 * wave + 16 * pg + 4 * g;
+      const uint32_t word = pack4_e4m3(clamp_fp8(div_by_scale(av[q][pg][0], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][1], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][2], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][3], s, rcp)));
+      *(uint32_t*)(args.aq_out + grow * I + i) = word;
+    }
+    if (wave == 0 && lane < 16) args.as_out[grow * (I >> 7) + j] = s;
+  }
+}
+
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
+  if (BM == 128) {
+    hipLaunchKernelGGL(moe_gemm2_pf_kernel, grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   switch (BM) {
     case 16: hipLaunchKernelGGL(moe_gemm2_kernel<16>, grid, block, 0, stream, a); break;
     case 32: hipLaunchKernelGGL(moe_gemm2_kernel<32>, grid, block, 0, stream, a); break;
@@ -440,18 +790,26 @@ static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, const float* w13s,
-                        const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
-                        int H, int I, int P, int top_k, int BM, int nblk, uint8_t* aq, float* as,
-                        hipStream_t stream) {
+hipError_t launch_gemm1(const uint8_t* xq, const void* xh, const float* xs, const uint8_t* w13,
+                        const float* w13s, const int32_t* sorted_ids, const int32_t* expert_ids,
+                        const int32_t* ntpp, const int32_t* eoff, int E, int H, int I, int P,
+                        int top_k, int BM, int nblk, uint8_t* aq, float* as, hipStream_t stream) {
   GemmArgs a{};
-  a.act = xq; a.act_scale = xs; a.w = w13; a.w_scale = w13s;
+  a.eoff = eoff; a.E = E;
+  a.act = xq; a.act_h = xh; a.act_scale = xs; a.w = w13; a.w_scale = w13s;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
   a.aq_out = aq; a.as_out = as;
   a.K = H; a.N = 2 * I; a.I = I; a.H = H; a.P = P; a.top_k = top_k;
   a.n_tiles = I / 128; a.nblk = nblk;
+  if (BM == 128) {
+    a.split = 2;
+    hipLaunchKernelGGL(moe_gemm1_pf_kernel, dim3((unsigned)(nblk * 2 * a.n_tiles)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
   const int rm = BM < 32 ? BM : 32;
   const int split = BM / rm;
+  a.split = split;
   const dim3 grid((unsigned)(nblk * split * a.n_tiles)), block(256);
   if (rm == 16)
     hipLaunchKernelGGL(moe_gemm1_kernel<16>, grid, block, 0, stream, a, BM, split);
@@ -464,9 +822,10 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
 
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
-                        const float* topk_w, int H, int I, int P, int BM, int nblk, uint16_t* y,
-                        hipStream_t stream) {
+                        const int32_t* eoff, int E, const float* topk_w, int H, int I, int P, int BM,
+                        int nblk, uint16_t* y, hipStream_t stream) {
   GemmArgs a{};
+  a.eoff = eoff; a.E = E; a.split = 1;
   a.act = aq; a.act_scale = as; a.w = w2; a.w_scale = w2s;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp; a.topk_w = topk_w;
   a.y_out = y;

@@ -76,6 +76,7 @@ def test_workspace_layout_is_disjoint_and_aligned():
         cap = -(-(P + E * (bm - 1)) // bm) * bm
         size = {"topk_ids": 4 * P, "topk_weights": 4 * P, "sorted_ids": 4 * cap,
                 "expert_ids": 4 * (cap // bm), "ntpp": 4, "xq": T * H, "xs": 4 * T * H // 128,
+                "xh": 2 * T * H,
                 "aq": cap * I, "as": 4 * cap * I // 128, "y": 2 * P * H, "align_scratch": 0}
         names = moe.TAPS
         for a, b in zip(names, names[1:]):
@@ -126,7 +127,7 @@ def test_stage_argument_checks():
     assert lib.moe_topk_softmax(None, 4, 8, 2, 1, vp(64), vp(128), None) == -1
     assert lib.moe_topk_softmax(None, 0, 8, 2, 1, None, None, None) == 0
     n = lib.moe_align_scratch_bytes(64, 8, 256)
-    assert n == 2 * 1 * 256 * 4
+    assert n == (2 * 1 * 256 + 257) * 4      # per-chunk counts + bases, expert offsets
     assert lib.moe_align(vp(16), 64, 8, 256, 24, vp(64), vp(128), vp(256), vp(512), n, None) == -2
     assert lib.moe_align(vp(16), 64, 8, 256, 16, vp(64), vp(128), vp(256), vp(512), n - 4, None) == -4
     assert lib.moe_align(None, 64, 8, 256, 16, vp(64), vp(128), vp(256), vp(512), n, None) == -1
