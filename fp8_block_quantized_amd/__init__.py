@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_fp8.so")
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIAS"}
-TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "xq", "xs", "xh",
+TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "xq", "xs", "a",
         "aq", "as", "y", "align_scratch"]
 MAX_EXPERTS = 512
 MAX_TOKENS = 16384
@@ -173,7 +173,6 @@ def workspace_taps(workspace, T, H, I, E, top_k):
         "ntpp": view("ntpp", torch.int32, (1,)),
         "xq": view("xq", torch.uint8, (T, H)),
         "xs": view("xs", torch.float32, (T, H // 128)),
-        "xh": view("xh", torch.float16, (T, H)),
         "aq": view("aq", torch.uint8, (cap, I)),
         "as": view("as", torch.float32, (cap, I // 128)),
         "y": view("y", torch.bfloat16, (P, H)),

@@ -42,7 +42,6 @@ namespace moe {
 
 struct GemmArgs {
   const uint8_t* act;        // GEMM1: xq [T, H]        GEMM2: aq [cap, I]
-  const void* act_h;         // GEMM1: f16 dec(xq) [T, H]
   const float* act_scale;    // GEMM1: xs [T, H/128]    GEMM2: as [cap, I/128]
   const uint8_t* w;          // GEMM1: w13 [E, 2I, H]   GEMM2: w2 [E, H, I]
   const float* w_scale;      // [E, N/128, K/128]
@@ -53,6 +52,7 @@ struct GemmArgs {
   uint8_t* aq_out;           // GEMM1: [cap, I]
   float* as_out;             // GEMM1: [cap, I/128]
   uint16_t* y_out;           // GEMM2: bf16 [P, H]
+  float* a_out;              // GEMM1 prefill: silu(gate) * up [cap, I] float32
   int K;                     // reduction length (H or I)
   int N;                     // weight rows per expert (2I or H)
   int I;
@@ -612,76 +612,77 @@ __global__ __launch_bounds__(256) void moe_gemm2_pf_kernel(GemmArgs args) {
   }
 }
 
-// GEMM1 prefill, with the exact partial sums of moe_gemm1_kernel: a 128-row
-// block is covered by two workgroups of 64 rows (a half that holds only
-// padding leaves at once); each workgroup takes 256 weight rows, the gate and
-// up rows of 128 features.  Weights stay e4m3 in the ring and are converted
-// to f16 after the LDS read; tokens arrive already as f16 (dec(xq), written
-// by the activation quantiser).  Wave w owns gate rows [32w, 32w+32) and the
-// matching up rows against all four token sub-tiles.
+// GEMM1 prefill, with the exact partial sums of moe_gemm1_kernel.  A
+// workgroup takes one 128-row block and 128 weight rows: the gate and up rows
+// of 64 features.  Each weight byte then serves 128 token rows and each token
+// byte 128 weight rows (128 FLOP per byte of L2 traffic, against 85 for 64 x
+// 256), the largest tile the float64 accumulators leave room for.  The four
+// waves split it 2 x 2 (64 tokens x 32 gate + 32 up rows each).  Both
+// operands stay e4m3 in a four-stage ring and are converted to f16 after the
+// LDS read, one 32-wide K chunk at a time; the four chained f16 MFMAs of a K
+// block accumulate in AGPRs.  The epilogue writes a = silu(gate) * up as
+// float32 (rounded once from float64); a requantisation kernel then computes
+// the 128-feature group scales, which span two workgroups here.
+constexpr int kPf1Stages = 4;
+constexpr int kPf1W = 128 * 128, kPf1A = 128 * 128, kPf1S = 1024;
+constexpr int kPf1Stage = kPf1W + kPf1A + kPf1S;
+constexpr int kPf1Loads = 9;               // DMA instructions per wave per stage
+
 __global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
-  constexpr int BM = 128, RM = 64;
-  constexpr int kA = RM * 256, kStage = kRingW + kA + kRingS;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingStages * kStage];
-  __shared__ float red[4][RM];
+  constexpr int BM = 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kPf1Stages * kPf1Stage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 1, wr = wave & 1;
   const int g = lane >> 4, l16 = lane & 15;
   const TileCoord tc = tile_of(blockIdx.x, args);
   if (!tc.valid) return;
-  const int b = tc.b, half = tc.half, j = tc.j;
-  const int row0 = b * BM + half * RM;
-  if (load_uniform(args.sorted_ids + row0) >= args.P) return;   // padding-only half
+  const int b = tc.b, j = tc.j;
   const int e = load_uniform(args.expert_ids + b);
-  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * j;
+  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 64 * j;
+  const int row0 = b * BM;
 
-  const uint8_t* wsrc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int pos = (wave * 8 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
-    const int wrow = r < 128 ? i0 + r : I + i0 + (r - 128);
-    wsrc[i] = args.w + ((size_t)e * args.N + wrow) * K + lc * 16;
-  }
-  const uint8_t* xh = (const uint8_t*)args.act_h;
+  const uint8_t* wsrc[4];
   const uint8_t* asrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 4, lc = (pos & 15) ^ (r & 15);
+    const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+    const int wrow = r < 64 ? i0 + r : I + i0 + (r - 64);
+    wsrc[i] = args.w + ((size_t)e * args.N + wrow) * K + lc * 16;
     const int p = args.sorted_ids[row0 + r];
-    const int t = p < args.P ? p / args.top_k : 0;   // padding rows: any valid row
-    asrc[i] = xh + (size_t)t * K * 2 + lc * 16;
+    asrc[i] = args.act + (size_t)(p < args.P ? p / args.top_k : 0) * K + lc * 16;
   }
   const float* ssrc;
   {
-    const int p = args.sorted_ids[row0 + lane];
+    const int p = args.sorted_ids[row0 + (wave & 1) * 64 + lane];
     ssrc = args.act_scale + (size_t)(p < args.P ? p / args.top_k : 0) * nkb;
   }
   auto issue = [&](int stage, int kb) {
-    const uint32_t base = lds_offset(ring + stage * kStage);
+    const uint32_t base = lds_offset(ring + stage * kPf1Stage);
+    const size_t ko = (size_t)kb * 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(wsrc[i] + (size_t)kb * 128, base + (wave * 8 + i) * 1024);
+    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + ko, base + (wave * 4 + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(asrc[i] + (size_t)kb * 256, base + kRingW + (wave * 4 + i) * 1024);
-    dma4(ssrc + kb, base + kRingW + kA + wave * 256);
+    for (int i = 0; i < 4; ++i) dma16(asrc[i] + ko, base + kPf1W + (wave * 4 + i) * 1024);
+    dma4(ssrc + kb, base + kPf1W + kPf1A + wave * 256);
   };
   const int nbn = args.N >> 7;
-  const float* wsg = args.w_scale + ((size_t)e * nbn + j) * nkb;
-  const float* wsu = args.w_scale + ((size_t)e * nbn + (I >> 7) + j) * nkb;
-  int poff[4][2], qoff[4][4];
+  const float* wsg = args.w_scale + ((size_t)e * nbn + (i0 >> 7)) * nkb;
+  const float* wsu = args.w_scale + ((size_t)e * nbn + ((I + i0) >> 7)) * nkb;
+  // LDS byte offsets of this lane's 8-byte operand pieces: row, 16-byte chunk
+  // (g + 4h) under the row's XOR swizzle; the chunk's second half is +8
+  int pw[4][2], pa[4][2];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
-    const int r = (pp < 2 ? 32 * wave + 16 * pp : 128 + 32 * wave + 16 * (pp - 2)) + l16;
-    poff[pp][0] = r * 128 + ((g ^ (r & 7)) << 4);
-    poff[pp][1] = r * 128 + (((g + 4) ^ (r & 7)) << 4);
+    const int r = (pp < 2 ? 32 * wr + 16 * pp : 64 + 32 * wr + 16 * (pp - 2)) + l16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pw[pp][h] = r * 128 + (((g + 4 * h) ^ (r & 7)) << 4);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int r = 16 * q + l16;
+    const int r = 64 * wt + 16 * q + l16;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = 2 * g + (c & 1) + 8 * (c >> 1);
-      qoff[q][c] = kRingW + r * 256 + ((idx ^ (r & 15)) << 4);
-    }
+    for (int h = 0; h < 2; ++h) pa[q][h] = kPf1W + r * 128 + (((g + 4 * h) ^ (r & 7)) << 4);
   }
   double acc[4][4][4];
 #pragma unroll
@@ -692,86 +693,90 @@ __global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
       for (int r = 0; r < 4; ++r) acc[pp][q][r] = 0.0;
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  if (nkb > 1) issue(1, 1);
+  auto frag = [](const uint8_t* p) {
+    const uint2 d = *(const uint2*)p;
+    _Float16 h[8];
+    e4m3x4_to_f16(d.x, h);
+    e4m3x4_to_f16(d.y, h + 4);
+    return *(const v8h*)h;
+  };
+
+#pragma unroll
+  for (int s0 = 0; s0 < kPf1Stages - 1; ++s0)
+    if (s0 < nkb) issue(s0, s0);
   for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) wait_vmem<kLoadsPerStage>(); else wait_vmem<0>();
+    // the oldest stage has landed once at most the younger ones are pending
+    const int younger = nkb - 1 - kb;
+    if (younger >= 2) wait_vmem<2 * kPf1Loads>();
+    else if (younger == 1) wait_vmem<kPf1Loads>();
+    else wait_vmem<0>();
     barrier_raw();
-    if (kb + 2 < nkb) issue((kb + 2) % kRingStages, kb + 2);
-    const uint8_t* st = ring + (kb % kRingStages) * kStage;
+    if (kb + kPf1Stages - 1 < nkb) issue((kb + kPf1Stages - 1) % kPf1Stages, kb + kPf1Stages - 1);
+    const uint8_t* st = ring + (kb % kPf1Stages) * kPf1Stage;
     const double swg = (double)load_uniform(wsg + kb), swu = (double)load_uniform(wsu + kb);
-    v8h wf[4][4];
+    v4f part[4][4];
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const uint4 a0 = *(const uint4*)(st + poff[pp][0]);
-      const uint4 a1 = *(const uint4*)(st + poff[pp][1]);
-      const uint32_t wd[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    for (int c = 0; c < 4; ++c) {
+      v8h wf[4], tf[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        _Float16 h[8];
-        e4m3x4_to_f16(wd[2 * c], h);
-        e4m3x4_to_f16(wd[2 * c + 1], h + 4);
-        wf[pp][c] = *(const v8h*)h;
-      }
+      for (int pp = 0; pp < 4; ++pp) wf[pp] = frag(st + pw[pp][c >> 1] + 8 * (c & 1));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tf[q] = frag(st + pa[q][c >> 1] + 8 * (c & 1));
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          part[pp][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp], tf[q], c == 0 ? zero : part[pp][q], 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v8h tq[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) tq[c] = *(const v8h*)(st + qoff[q][c]);
-      const double sad = (double)*(const float*)(st + kRingW + kA + (16 * q + l16) * 4);
+      const double sad = (double)*(const float*)(st + kPf1W + kPf1A + (64 * wt + 16 * q + l16) * 4);
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        v4f part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][0], tq[0], zero, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][1], tq[1], part, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][2], tq[2], part, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp][3], tq[3], part, 0, 0, 0);
         const double sc = sad * (pp < 2 ? swg : swu);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fma((double)part[r], sc, acc[pp][q][r]);
+        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fma((double)part[pp][q][r], sc, acc[pp][q][r]);
       }
     }
   }
-
-  // a = silu(gate) * up in float64, rounded once to float32, requantised per
-  // row over the 128 features of tile j
-  float av[4][2][4];
+  // a = silu(gate) * up in float64, rounded once to float32, sorted order
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    float m = 0.0f;
+    float* arow = args.a_out + (size_t)(row0 + 64 * wt + 16 * q + l16) * I;
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
+    for (int pg = 0; pg < 2; ++pg) {
+      float4 v;
+      float* vp = (float*)&v;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const double gt = acc[pg][q][r], up = acc[pg + 2][q][r];
-        const float a = (float)(gt / (1.0 + exp(-gt)) * up);
-        av[q][pg][r] = a;
-        m = __builtin_fmaxf(m, __builtin_fabsf(a));
+        vp[r] = (float)(gt / (1.0 + exp(-gt)) * up);
       }
-    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
-    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
-    if (lane < 16) red[wave][16 * q + l16] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int rq = 16 * q + l16;
-    const float amax = __builtin_fmaxf(__builtin_fmaxf(red[0][rq], red[1][rq]),
-                                       __builtin_fmaxf(red[2][rq], red[3][rq]));
-    float s, rcp;
-    group_scale(amax, s, rcp);
-    const size_t grow = (size_t)(row0 + rq);
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      const int i = i0 + 32 * wave + 16 * pg + 4 * g;
-      const uint32_t word = pack4_e4m3(clamp_fp8(div_by_scale(av[q][pg][0], s, rcp)),
-                                       clamp_fp8(div_by_scale(av[q][pg][1], s, rcp)),
-                                       clamp_fp8(div_by_scale(av[q][pg][2], s, rcp)),
-                                       clamp_fp8(div_by_scale(av[q][pg][3], s, rcp)));
-      *(uint32_t*)(args.aq_out + grow * I + i) = word;
+      *(float4*)(arow + i0 + 32 * wr + 16 * pg + 4 * g) = v;
     }
-    if (wave == 0 && lane < 16) args.as_out[grow * (I >> 7) + j] = s;
   }
+}
+
+// Requantisation of a [rows, I] float32 (sorted order) to e4m3 codes and
+// 128-group scales, for the rows in use: the per-token group quantiser of the
+// activations, on float32 input.  32 lanes own a group (4 values each).
+__global__ __launch_bounds__(256) void requant_rows_kernel(const float4* __restrict__ a,
+                                                           const int32_t* __restrict__ ntpp,
+                                                           int I, uint32_t* __restrict__ aq,
+                                                           float* __restrict__ as) {
+  const long long slot = (long long)blockIdx.x * 256 + threadIdx.x;   // 4 values per slot
+  const int per_row = I >> 2;
+  const long long row = slot / per_row;
+  if (row * per_row >= (long long)load_uniform(ntpp) * per_row) return;   // whole wave
+  const float4 v = a[slot];
+  float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                               __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
+  amax = wave_max_xor(amax, 16, 1);    // the 32 lanes of this group
+  float s, r;
+  group_scale(amax, s, r);
+  aq[slot] = pack4_e4m3(clamp_fp8(div_by_scale(v.x, s, r)), clamp_fp8(div_by_scale(v.y, s, r)),
+                        clamp_fp8(div_by_scale(v.z, s, r)), clamp_fp8(div_by_scale(v.w, s, r)));
+  if ((threadIdx.x & 31) == 0) as[slot >> 5] = s;
 }
 
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
@@ -790,23 +795,27 @@ static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_gemm1(const uint8_t* xq, const void* xh, const float* xs, const uint8_t* w13,
-                        const float* w13s, const int32_t* sorted_ids, const int32_t* expert_ids,
-                        const int32_t* ntpp, const int32_t* eoff, int E, int H, int I, int P,
-                        int top_k, int BM, int nblk, uint8_t* aq, float* as, hipStream_t stream) {
+hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, const float* w13s,
+                        const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
+                        const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
+                        float* a_buf, uint8_t* aq, float* as, hipStream_t stream) {
   GemmArgs a{};
   a.eoff = eoff; a.E = E;
-  a.act = xq; a.act_h = xh; a.act_scale = xs; a.w = w13; a.w_scale = w13s;
+  a.act = xq; a.act_scale = xs; a.w = w13; a.w_scale = w13s;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
-  a.aq_out = aq; a.as_out = as;
+  a.aq_out = aq; a.as_out = as; a.a_out = a_buf;
   a.K = H; a.N = 2 * I; a.I = I; a.H = H; a.P = P; a.top_k = top_k;
-  a.n_tiles = I / 128; a.nblk = nblk;
+  a.nblk = nblk;
   if (BM == 128) {
-    a.split = 2;
-    hipLaunchKernelGGL(moe_gemm1_pf_kernel, dim3((unsigned)(nblk * 2 * a.n_tiles)), dim3(256), 0,
-                       stream, a);
+    a.split = 1;
+    a.n_tiles = I / 64;
+    hipLaunchKernelGGL(moe_gemm1_pf_kernel, dim3((unsigned)(nblk * a.n_tiles)), dim3(256), 0, stream, a);
+    const long long slots = (long long)nblk * BM * (I / 4);
+    hipLaunchKernelGGL(requant_rows_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
+                       stream, (const float4*)a_buf, ntpp, I, (uint32_t*)aq, as);
     return hipGetLastError();
   }
+  a.n_tiles = I / 128;
   const int rm = BM < 32 ? BM : 32;
   const int split = BM / rm;
   a.split = split;

@@ -8,17 +8,17 @@
 namespace moe {
 
 hipError_t launch_group_quant(const void* x, long long M, int K, uint8_t* q, float* s,
-                              void* deq_f16, hipStream_t stream);
+                              hipStream_t stream);
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int top_k, int renormalize,
                                int32_t* ids, float* w, hipStream_t stream);
 size_t align_scratch_bytes(int P, int E);
 const int32_t* align_expert_offsets(const void* scratch, int P, int E);
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
                         int32_t* expert_ids, int32_t* ntpp, void* scratch, hipStream_t stream);
-hipError_t launch_gemm1(const uint8_t* xq, const void* xh, const float* xs, const uint8_t* w13,
-                        const float* w13s, const int32_t* sorted_ids, const int32_t* expert_ids,
-                        const int32_t* ntpp, const int32_t* eoff, int E, int H, int I, int P,
-                        int top_k, int BM, int nblk, uint8_t* aq, float* as, hipStream_t stream);
+hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, const float* w13s,
+                        const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
+                        const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
+                        float* a_buf, uint8_t* aq, float* as, hipStream_t stream);
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, const float* topk_w, int H, int I, int P, int BM,

@@ -18,12 +18,10 @@
 
 namespace moe {
 
-// With `deq` non-null the kernel also writes dec(q) as f16 (exact: every e4m3
-// value is an f16 value), the token operand of the f16-MFMA GEMM1.
 template <int SLOTS>
 __global__ __launch_bounds__(256) void group_quant_bf16_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scales,
-    uint4* __restrict__ deq, long long nslots) {
+    long long nslots) {
   // slot = one lane's 8 elements; 16 slots per group
   const long long base = ((long long)blockIdx.x * 256 * SLOTS) + threadIdx.x;
   uint4 v[SLOTS];
@@ -54,25 +52,19 @@ __global__ __launch_bounds__(256) void group_quant_bf16_kernel(
     if (slot < nslots) {
       q[slot] = out;
       if ((threadIdx.x & 15) == 0) scales[slot >> 4] = s;
-      if (deq) {
-        _Float16 h[8];
-        e4m3x4_to_f16(out.x, h);
-        e4m3x4_to_f16(out.y, h + 4);
-        deq[slot] = *(const uint4*)h;
-      }
     }
   }
 }
 
 hipError_t launch_group_quant(const void* x, long long M, int K, uint8_t* q, float* s,
-                              void* deq_f16, hipStream_t stream) {
+                              hipStream_t stream) {
   const long long nslots = M * (long long)(K / 8);
   if (nslots == 0) return hipSuccess;
   constexpr int SLOTS = 2;
   const long long per_block = 256LL * SLOTS;
   const long long nblk = (nslots + per_block - 1) / per_block;
   hipLaunchKernelGGL(group_quant_bf16_kernel<SLOTS>, dim3((unsigned)nblk), dim3(256), 0, stream,
-                     (const uint4*)x, (uint2*)q, s, (uint4*)deq_f16, nslots);
+                     (const uint4*)x, (uint2*)q, s, nslots);
   return hipGetLastError();
 }
 
