@@ -500,17 +500,20 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
 // ---------------------------------------------------------------------------
 constexpr int kRingStages = 3;
 constexpr int kRingW = 256 * 128;      // 256 weight rows x one 128-byte K block
-constexpr int kRingS = 1024;           // token scales (four 256-byte wave slots)
-constexpr int kLoadsPerStage = 13;     // DMA instructions per wave per stage
 
-// GEMM2 prefill: 128 sorted rows x 256 output features per workgroup; wave w
-// owns features [64w, 64w+64) (4 MFMA rows) against all 8 token sub-tiles.
-__global__ __launch_bounds__(256) void moe_gemm2_pf_kernel(GemmArgs args) {
+// GEMM2 prefill: 128 sorted rows x 256 output features per workgroup, eight
+// waves (two per SIMD, so one wave's scale FMAs overlap the other's MFMAs);
+// wave w owns tokens [64 (w>>2), +64) x features [64 (w&3), +64).
+constexpr int kPf2Loads = 7;               // DMA instructions per wave per stage
+constexpr int kPf2S = 2048;                // token scales, eight 256-byte wave slots
+
+__global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   constexpr int BM = 128;
-  constexpr int kA = BM * 128, kStage = kRingW + kA + kRingS;
+  constexpr int kA = BM * 128, kStage = kRingW + kA + kPf2S;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingStages * kStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 2, wf = wave & 3;
   const int g = lane >> 4, l16 = lane & 15;
   const TileCoord tc = tile_of(blockIdx.x, args);
   if (!tc.valid) return;
@@ -519,17 +522,17 @@ __global__ __launch_bounds__(256) void moe_gemm2_pf_kernel(GemmArgs args) {
   const int K = args.K, nkb = K >> 7;
   const int row0 = b * BM, n0 = 256 * j;
 
-  const uint8_t* wsrc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int pos = (wave * 8 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
-    const int row = n0 + r < args.N ? n0 + r : 0;    // rows past H: any valid row, never stored
-    wsrc[i] = args.w + ((size_t)e * args.N + row) * K + lc * 16;
-  }
-  const uint8_t* asrc[4];
+  const uint8_t* wsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+    const int row = n0 + r < args.N ? n0 + r : 0;    // rows past H: any valid row, never stored
+    wsrc[i] = args.w + ((size_t)e * args.N + row) * K + lc * 16;
+  }
+  const uint8_t* asrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pos = (wave * 2 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
     asrc[i] = args.act + (size_t)(row0 + r) * K + lc * 16;
   }
   const float* ssrc = args.act_scale + (size_t)(row0 + (wave & 1) * 64 + lane) * nkb;
@@ -537,37 +540,37 @@ __global__ __launch_bounds__(256) void moe_gemm2_pf_kernel(GemmArgs args) {
     const uint32_t base = lds_offset(ring + stage * kStage);
     const size_t ko = (size_t)kb * 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(wsrc[i] + ko, base + (wave * 8 + i) * 1024);
+    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + ko, base + (wave * 4 + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(asrc[i] + ko, base + kRingW + (wave * 4 + i) * 1024);
+    for (int i = 0; i < 2; ++i) dma16(asrc[i] + ko, base + kRingW + (wave * 2 + i) * 1024);
     dma4(ssrc + kb, base + kRingW + kA + wave * 256);
   };
-  const float* wsp = args.w_scale +
-      ((size_t)e * (args.N >> 7) + ((n0 + 64 * wave < args.N ? n0 + 64 * wave : 0) >> 7)) * nkb;
-  int poff[4][2], qoff[8][2];
+  const int nf = n0 + 64 * wf;
+  const float* wsp = args.w_scale + ((size_t)e * (args.N >> 7) + ((nf < args.N ? nf : 0) >> 7)) * nkb;
+  int poff[4][2], qoff[4][2];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
-    const int r = 64 * wave + 16 * pp + l16;
+    const int r = 64 * wf + 16 * pp + l16;
     poff[pp][0] = r * 128 + ((g ^ (r & 7)) << 4);
     poff[pp][1] = r * 128 + (((g + 4) ^ (r & 7)) << 4);
   }
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = 16 * q + l16;
+  for (int q = 0; q < 4; ++q) {
+    const int r = 64 * wt + 16 * q + l16;
     qoff[q][0] = kRingW + r * 128 + ((g ^ (r & 7)) << 4);
     qoff[q][1] = kRingW + r * 128 + (((g + 4) ^ (r & 7)) << 4);
   }
-  v4f acc[4][8];
+  v4f acc[4][4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 4; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
   issue(0, 0);
   if (nkb > 1) issue(1, 1);
   for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) wait_vmem<kLoadsPerStage>(); else wait_vmem<0>();
+    if (kb + 1 < nkb) wait_vmem<kPf2Loads>(); else wait_vmem<0>();
     barrier_raw();
     if (kb + 2 < nkb) issue((kb + 2) % kRingStages, kb + 2);
     const uint8_t* st = ring + (kb % kRingStages) * kStage;
@@ -580,11 +583,11 @@ __global__ __launch_bounds__(256) void moe_gemm2_pf_kernel(GemmArgs args) {
       pf[pp] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const uint4 b0 = *(const uint4*)(st + qoff[q][0]);
       const uint4 b1 = *(const uint4*)(st + qoff[q][1]);
       const v8i bq = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-      const float sc = *(const float*)(st + kRingW + kA + (16 * q + l16) * 4) * sw;
+      const float sc = *(const float*)(st + kRingW + kA + (64 * wt + 16 * q + l16) * 4) * sw;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
         const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf[pp], bq, zero, 0, 0, 0, 0, 0, 0);
@@ -595,18 +598,18 @@ __global__ __launch_bounds__(256) void moe_gemm2_pf_kernel(GemmArgs args) {
   }
   // y[p] = routing weight * acc, bf16, in pair order (real rows only)
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int p = args.sorted_ids[row0 + 16 * q + l16];
+  for (int q = 0; q < 4; ++q) {
+    const int p = args.sorted_ids[row0 + 64 * wt + 16 * q + l16];
     if (p >= args.P) continue;
-    const float wt = args.topk_w[p];
+    const float wt_p = args.topk_w[p];
     uint16_t* yrow = args.y_out + (size_t)p * args.H;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const int h0 = n0 + 64 * wave + 16 * pp + 4 * g;
+      const int h0 = nf + 16 * pp + 4 * g;
       if (h0 >= args.H) continue;
       uint2 v;
-      v.x = f32_to_bf16_bits(acc[pp][q][0] * wt) | (f32_to_bf16_bits(acc[pp][q][1] * wt) << 16);
-      v.y = f32_to_bf16_bits(acc[pp][q][2] * wt) | (f32_to_bf16_bits(acc[pp][q][3] * wt) << 16);
+      v.x = f32_to_bf16_bits(acc[pp][q][0] * wt_p) | (f32_to_bf16_bits(acc[pp][q][1] * wt_p) << 16);
+      v.y = f32_to_bf16_bits(acc[pp][q][2] * wt_p) | (f32_to_bf16_bits(acc[pp][q][3] * wt_p) << 16);
       *(uint2*)(yrow + h0) = v;
     }
   }
@@ -616,19 +619,20 @@ __global__ __launch_bounds__(256) void moe_gemm2_pf_kernel(GemmArgs args) {
 // workgroup takes one 128-row block and 128 weight rows: the gate and up rows
 // of 64 features.  Each weight byte then serves 128 token rows and each token
 // byte 128 weight rows (128 FLOP per byte of L2 traffic, against 85 for 64 x
-// 256), the largest tile the float64 accumulators leave room for.  The four
-// waves split it 2 x 2 (64 tokens x 32 gate + 32 up rows each).  Both
+// 256), the largest tile the float64 accumulators leave room for.  Eight
+// waves (two per SIMD, so one wave's conversions and float64 FMAs overlap the
+// other's MFMAs) split it 4 x 2: 32 tokens x (32 gate + 32 up rows).  Both
 // operands stay e4m3 in a four-stage ring and are converted to f16 after the
 // LDS read, one 32-wide K chunk at a time; the four chained f16 MFMAs of a K
 // block accumulate in AGPRs.  The epilogue writes a = silu(gate) * up as
 // float32 (rounded once from float64); a requantisation kernel then computes
 // the 128-feature group scales, which span two workgroups here.
 constexpr int kPf1Stages = 4;
-constexpr int kPf1W = 128 * 128, kPf1A = 128 * 128, kPf1S = 1024;
+constexpr int kPf1W = 128 * 128, kPf1A = 128 * 128, kPf1S = 2048;
 constexpr int kPf1Stage = kPf1W + kPf1A + kPf1S;
-constexpr int kPf1Loads = 9;               // DMA instructions per wave per stage
+constexpr int kPf1Loads = 5;               // DMA instructions per wave per stage
 
-__global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
+__global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
   constexpr int BM = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kPf1Stages * kPf1Stage];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -642,11 +646,11 @@ __global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
   const int K = args.K, nkb = K >> 7, I = args.I, i0 = 64 * j;
   const int row0 = b * BM;
 
-  const uint8_t* wsrc[4];
-  const uint8_t* asrc[4];
+  const uint8_t* wsrc[2];
+  const uint8_t* asrc[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+  for (int i = 0; i < 2; ++i) {
+    const int pos = (wave * 2 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
     const int wrow = r < 64 ? i0 + r : I + i0 + (r - 64);
     wsrc[i] = args.w + ((size_t)e * args.N + wrow) * K + lc * 16;
     const int p = args.sorted_ids[row0 + r];
@@ -661,9 +665,9 @@ __global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
     const uint32_t base = lds_offset(ring + stage * kPf1Stage);
     const size_t ko = (size_t)kb * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + ko, base + (wave * 4 + i) * 1024);
+    for (int i = 0; i < 2; ++i) dma16(wsrc[i] + ko, base + (wave * 2 + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(asrc[i] + ko, base + kPf1W + (wave * 4 + i) * 1024);
+    for (int i = 0; i < 2; ++i) dma16(asrc[i] + ko, base + kPf1W + (wave * 2 + i) * 1024);
     dma4(ssrc + kb, base + kPf1W + kPf1A + wave * 256);
   };
   const int nbn = args.N >> 7;
@@ -671,7 +675,7 @@ __global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
   const float* wsu = args.w_scale + ((size_t)e * nbn + ((I + i0) >> 7)) * nkb;
   // LDS byte offsets of this lane's 8-byte operand pieces: row, 16-byte chunk
   // (g + 4h) under the row's XOR swizzle; the chunk's second half is +8
-  int pw[4][2], pa[4][2];
+  int pw[4][2], pa[2][2];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
     const int r = (pp < 2 ? 32 * wr + 16 * pp : 64 + 32 * wr + 16 * (pp - 2)) + l16;
@@ -679,16 +683,16 @@ __global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
     for (int h = 0; h < 2; ++h) pw[pp][h] = r * 128 + (((g + 4 * h) ^ (r & 7)) << 4);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 64 * wt + 16 * q + l16;
+  for (int q = 0; q < 2; ++q) {
+    const int r = 32 * wt + 16 * q + l16;
 #pragma unroll
     for (int h = 0; h < 2; ++h) pa[q][h] = kPf1W + r * 128 + (((g + 4 * h) ^ (r & 7)) << 4);
   }
-  double acc[4][4][4];
+  double acc[4][2][4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[pp][q][r] = 0.0;
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -714,35 +718,37 @@ __global__ __launch_bounds__(256) void moe_gemm1_pf_kernel(GemmArgs args) {
     if (kb + kPf1Stages - 1 < nkb) issue((kb + kPf1Stages - 1) % kPf1Stages, kb + kPf1Stages - 1);
     const uint8_t* st = ring + (kb % kPf1Stages) * kPf1Stage;
     const double swg = (double)load_uniform(wsg + kb), swu = (double)load_uniform(wsu + kb);
-    v4f part[4][4];
+    double sad[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      sad[q] = (double)*(const float*)(st + kPf1W + kPf1A + (32 * wt + 16 * q + l16) * 4);
+    v4f part[4][2];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      v8h wf[4], tf[4];
+      v8h wf[4], tf[2];
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) wf[pp] = frag(st + pw[pp][c >> 1] + 8 * (c & 1));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tf[q] = frag(st + pa[q][c >> 1] + 8 * (c & 1));
+      for (int q = 0; q < 2; ++q) tf[q] = frag(st + pa[q][c >> 1] + 8 * (c & 1));
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 2; ++q)
           part[pp][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp], tf[q], c == 0 ? zero : part[pp][q], 0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double sad = (double)*(const float*)(st + kPf1W + kPf1A + (64 * wt + 16 * q + l16) * 4);
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        const double sc = sad * (pp < 2 ? swg : swu);
+        const double sc = sad[q] * (pp < 2 ? swg : swu);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fma((double)part[pp][q][r], sc, acc[pp][q][r]);
       }
-    }
   }
   // a = silu(gate) * up in float64, rounded once to float32, sorted order
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float* arow = args.a_out + (size_t)(row0 + 64 * wt + 16 * q + l16) * I;
+  for (int q = 0; q < 2; ++q) {
+    float* arow = args.a_out + (size_t)(row0 + 32 * wt + 16 * q + l16) * I;
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       float4 v;
@@ -782,7 +788,7 @@ __global__ __launch_bounds__(256) void requant_rows_kernel(const float4* __restr
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
   if (BM == 128) {
-    hipLaunchKernelGGL(moe_gemm2_pf_kernel, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(moe_gemm2_pf_kernel, grid, dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   switch (BM) {
@@ -809,7 +815,7 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
   if (BM == 128) {
     a.split = 1;
     a.n_tiles = I / 64;
-    hipLaunchKernelGGL(moe_gemm1_pf_kernel, dim3((unsigned)(nblk * a.n_tiles)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(moe_gemm1_pf_kernel, dim3((unsigned)(nblk * a.n_tiles)), dim3(512), 0, stream, a);
     const long long slots = (long long)nblk * BM * (I / 4);
     hipLaunchKernelGGL(requant_rows_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
                        stream, (const float4*)a_buf, ntpp, I, (uint32_t*)aq, as);
