@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_fp8.so")
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIAS"}
-TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "xq", "xs", "a",
-        "aq", "as", "y", "align_scratch"]
+TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "xq", "xs", "aq",
+        "as", "y", "align_scratch"]
 MAX_EXPERTS = 512
 MAX_TOKENS = 16384
 MAX_TOP_K = 32

@@ -52,7 +52,6 @@ struct GemmArgs {
   uint8_t* aq_out;           // GEMM1: [cap, I]
   float* as_out;             // GEMM1: [cap, I/128]
   uint16_t* y_out;           // GEMM2: bf16 [P, H]
-  float* a_out;              // GEMM1 prefill: silu(gate) * up [cap, I] float32
   int K;                     // reduction length (H or I)
   int N;                     // weight rows per expert (2I or H)
   int I;
@@ -615,44 +614,53 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   }
 }
 
-// GEMM1 prefill, with the exact partial sums of moe_gemm1_kernel.  A
-// workgroup takes one 128-row block and 128 weight rows: the gate and up rows
-// of 64 features.  Each weight byte then serves 128 token rows and each token
-// byte 128 weight rows (128 FLOP per byte of L2 traffic, against 85 for 64 x
-// 256), the largest tile the float64 accumulators leave room for.  Eight
-// waves (two per SIMD, so one wave's conversions and float64 FMAs overlap the
-// other's MFMAs) split it 4 x 2: 32 tokens x (32 gate + 32 up rows).  Both
-// operands stay e4m3 in a four-stage ring and are converted to f16 after the
-// LDS read, one 32-wide K chunk at a time; the four chained f16 MFMAs of a K
-// block accumulate in AGPRs.  The epilogue writes a = silu(gate) * up as
-// float32 (rounded once from float64); a requantisation kernel then computes
-// the 128-feature group scales, which span two workgroups here.
-constexpr int kPf1Stages = 4;
-constexpr int kPf1W = 128 * 128, kPf1A = 128 * 128, kPf1S = 2048;
+// GEMM1 prefill.  A workgroup takes one 128-row block and 128 features: the
+// 128 gate rows and 128 up rows of w13 that feed them, which is one whole
+// requantisation group, so SiLU*mul and the requant run in the epilogue.
+// Eight waves (two per SIMD: one wave's conversions and scale folds overlap
+// the other's MFMAs) split the tile 2 x 4: 64 tokens x (32 gate + 32 up
+// features).  Per 128-wide K block a wave converts 8 e4m3 fragments per
+// 32-wide chunk to f16 and issues 16 chained v_mfma_f32_16x16x32_f16; its
+// conversions grow with the wave tile's edges and its MFMAs with the area,
+// and 64 x 64 is the largest tile whose float32 accumulators and block
+// partials fit two waves per SIMD.  Each block partial (exact to ~1e-10 of
+// sum |p|, as in moe_gemm1_kernel) is scaled by xs * ws and added into a
+// float32 accumulator: the order of the oracle's kernel reading, with a
+// relative error of a few 1e-7, far below one e4m3 step of a.  Operands stay
+// e4m3 in a three-stage LDS ring filled by direct global->LDS loads (XOR
+// swizzle on 16-byte chunks, no bank conflicts on the 16-byte reads).
+constexpr int kPf1Stages = 3;
+constexpr int kPf1W = 256 * 128, kPf1A = 128 * 128, kPf1S = 2048;
 constexpr int kPf1Stage = kPf1W + kPf1A + kPf1S;
-constexpr int kPf1Loads = 5;               // DMA instructions per wave per stage
+constexpr int kPf1Loads = 7;               // DMA instructions per wave per stage
 
 __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
   constexpr int BM = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kPf1Stages * kPf1Stage];
+  __shared__ float red[2][4][64];           // per-token amax of each wave's 32 features
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wt = wave >> 1, wr = wave & 1;
+  const int wt = wave >> 2, wr = wave & 3;
   const int g = lane >> 4, l16 = lane & 15;
   const TileCoord tc = tile_of(blockIdx.x, args);
   if (!tc.valid) return;
   const int b = tc.b, j = tc.j;
   const int e = load_uniform(args.expert_ids + b);
-  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 64 * j;
+  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * j;
   const int row0 = b * BM;
 
-  const uint8_t* wsrc[2];
+  // this lane's share of a stage: 4 x 16 bytes of weights, 2 x 16 of tokens
+  const uint8_t* wsrc[4];
   const uint8_t* asrc[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+    const int wrow = r < 128 ? i0 + r : I + i0 + (r - 128);
+    wsrc[i] = args.w + ((size_t)e * args.N + wrow) * K + lc * 16;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int pos = (wave * 2 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
-    const int wrow = r < 64 ? i0 + r : I + i0 + (r - 64);
-    wsrc[i] = args.w + ((size_t)e * args.N + wrow) * K + lc * 16;
     const int p = args.sorted_ids[row0 + r];
     asrc[i] = args.act + (size_t)(p < args.P ? p / args.top_k : 0) * K + lc * 16;
   }
@@ -661,40 +669,40 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
     const int p = args.sorted_ids[row0 + (wave & 1) * 64 + lane];
     ssrc = args.act_scale + (size_t)(p < args.P ? p / args.top_k : 0) * nkb;
   }
+  // the token scales of rows 0..127 land in slots 0 and 1; the other waves'
+  // copies fill unused slots and keep every wave's load count equal
   auto issue = [&](int stage, int kb) {
     const uint32_t base = lds_offset(ring + stage * kPf1Stage);
     const size_t ko = (size_t)kb * 128;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(wsrc[i] + ko, base + (wave * 2 + i) * 1024);
+    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + ko, base + (wave * 4 + i) * 1024);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(asrc[i] + ko, base + kPf1W + (wave * 2 + i) * 1024);
     dma4(ssrc + kb, base + kPf1W + kPf1A + wave * 256);
   };
   const int nbn = args.N >> 7;
-  const float* wsg = args.w_scale + ((size_t)e * nbn + (i0 >> 7)) * nkb;
+  const float* wsg = args.w_scale + ((size_t)e * nbn + j) * nkb;
   const float* wsu = args.w_scale + ((size_t)e * nbn + ((I + i0) >> 7)) * nkb;
   // LDS byte offsets of this lane's 8-byte operand pieces: row, 16-byte chunk
   // (g + 4h) under the row's XOR swizzle; the chunk's second half is +8
-  int pw[4][2], pa[2][2];
+  int pw[4][2], pa[4][2];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
-    const int r = (pp < 2 ? 32 * wr + 16 * pp : 64 + 32 * wr + 16 * (pp - 2)) + l16;
+    const int r = (pp < 2 ? 32 * wr + 16 * pp : 128 + 32 * wr + 16 * (pp - 2)) + l16;
 #pragma unroll
     for (int h = 0; h < 2; ++h) pw[pp][h] = r * 128 + (((g + 4 * h) ^ (r & 7)) << 4);
   }
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 32 * wt + 16 * q + l16;
+  for (int q = 0; q < 4; ++q) {
+    const int r = 64 * wt + 16 * q + l16;
 #pragma unroll
     for (int h = 0; h < 2; ++h) pa[q][h] = kPf1W + r * 128 + (((g + 4 * h) ^ (r & 7)) << 4);
   }
-  double acc[4][2][4];
+  v4f acc[4][4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[pp][q][r] = 0.0;
+    for (int q = 0; q < 4; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
   auto frag = [](const uint8_t* p) {
@@ -705,84 +713,81 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
     return *(const v8h*)h;
   };
 
-#pragma unroll
-  for (int s0 = 0; s0 < kPf1Stages - 1; ++s0)
-    if (s0 < nkb) issue(s0, s0);
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
   for (int kb = 0; kb < nkb; ++kb) {
-    // the oldest stage has landed once at most the younger ones are pending
-    const int younger = nkb - 1 - kb;
-    if (younger >= 2) wait_vmem<2 * kPf1Loads>();
-    else if (younger == 1) wait_vmem<kPf1Loads>();
-    else wait_vmem<0>();
+    // stage kb has landed once at most the next stage's loads are pending
+    if (kb + 1 < nkb) wait_vmem<kPf1Loads>(); else wait_vmem<0>();
     barrier_raw();
-    if (kb + kPf1Stages - 1 < nkb) issue((kb + kPf1Stages - 1) % kPf1Stages, kb + kPf1Stages - 1);
+    if (kb + 2 < nkb) issue((kb + 2) % kPf1Stages, kb + 2);
     const uint8_t* st = ring + (kb % kPf1Stages) * kPf1Stage;
-    const double swg = (double)load_uniform(wsg + kb), swu = (double)load_uniform(wsu + kb);
-    double sad[2];
+    const float swg = load_uniform(wsg + kb), swu = load_uniform(wsu + kb);
+    float sa[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      sad[q] = (double)*(const float*)(st + kPf1W + kPf1A + (32 * wt + 16 * q + l16) * 4);
-    v4f part[4][2];
+    for (int q = 0; q < 4; ++q) sa[q] = *(const float*)(st + kPf1W + kPf1A + (64 * wt + 16 * q + l16) * 4);
+    v4f part[4][4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      v8h wf[4], tf[2];
+      v8h wf[4], tf[4];
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) wf[pp] = frag(st + pw[pp][c >> 1] + 8 * (c & 1));
 #pragma unroll
-      for (int q = 0; q < 2; ++q) tf[q] = frag(st + pa[q][c >> 1] + 8 * (c & 1));
+      for (int q = 0; q < 4; ++q) tf[q] = frag(st + pa[q][c >> 1] + 8 * (c & 1));
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < 4; ++q)
           part[pp][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp], tf[q], c == 0 ? zero : part[pp][q], 0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        const double sc = sad[q] * (pp < 2 ? swg : swu);
+        const float sc = sa[q] * (pp < 2 ? swg : swu);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fma((double)part[pp][q][r], sc, acc[pp][q][r]);
+        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[pp][q][r], sc, acc[pp][q][r]);
       }
   }
-  // a = silu(gate) * up in float64, rounded once to float32, sorted order
+
+  // a = silu(gate) * up in float32, then the per-row requant over the 128
+  // features of tile j: amax across the wave's lanes, then across its 4 waves
+  float av[4][2][4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    float* arow = args.a_out + (size_t)(row0 + 32 * wt + 16 * q + l16) * I;
+  for (int q = 0; q < 4; ++q) {
+    float m = 0.0f;
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      float4 v;
-      float* vp = (float*)&v;
+    for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const double gt = acc[pg][q][r], up = acc[pg + 2][q][r];
-        vp[r] = (float)(gt / (1.0 + exp(-gt)) * up);
+        const float gt = acc[pg][q][r], up = acc[pg + 2][q][r];
+        const float a = gt / (1.0f + expf(-gt)) * up;
+        av[q][pg][r] = a;
+        m = __builtin_fmaxf(m, __builtin_fabsf(a));
       }
-      *(float4*)(arow + i0 + 32 * wr + 16 * pg + 4 * g) = v;
-    }
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+    if (lane < 16) red[wt][wr][16 * q + l16] = m;
   }
-}
-
-// Requantisation of a [rows, I] float32 (sorted order) to e4m3 codes and
-// 128-group scales, for the rows in use: the per-token group quantiser of the
-// activations, on float32 input.  32 lanes own a group (4 values each).
-__global__ __launch_bounds__(256) void requant_rows_kernel(const float4* __restrict__ a,
-                                                           const int32_t* __restrict__ ntpp,
-                                                           int I, uint32_t* __restrict__ aq,
-                                                           float* __restrict__ as) {
-  const long long slot = (long long)blockIdx.x * 256 + threadIdx.x;   // 4 values per slot
-  const int per_row = I >> 2;
-  const long long row = slot / per_row;
-  if (row * per_row >= (long long)load_uniform(ntpp) * per_row) return;   // whole wave
-  const float4 v = a[slot];
-  float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
-                               __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
-  amax = wave_max_xor(amax, 16, 1);    // the 32 lanes of this group
-  float s, r;
-  group_scale(amax, s, r);
-  aq[slot] = pack4_e4m3(clamp_fp8(div_by_scale(v.x, s, r)), clamp_fp8(div_by_scale(v.y, s, r)),
-                        clamp_fp8(div_by_scale(v.z, s, r)), clamp_fp8(div_by_scale(v.w, s, r)));
-  if ((threadIdx.x & 31) == 0) as[slot >> 5] = s;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rq = 16 * q + l16;
+    const float amax = __builtin_fmaxf(__builtin_fmaxf(red[wt][0][rq], red[wt][1][rq]),
+                                       __builtin_fmaxf(red[wt][2][rq], red[wt][3][rq]));
+    float s, rcp;
+    group_scale(amax, s, rcp);
+    const size_t grow = (size_t)(row0 + 64 * wt + rq);
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const int i = i0 + 32 * wr + 16 * pg + 4 * g;
+      const uint32_t word = pack4_e4m3(clamp_fp8(div_by_scale(av[q][pg][0], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][1], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][2], s, rcp)),
+                                       clamp_fp8(div_by_scale(av[q][pg][3], s, rcp)));
+      *(uint32_t*)(args.aq_out + grow * I + i) = word;
+    }
+    if (wr == 0 && lane < 16) args.as_out[grow * (I >> 7) + j] = s;
+  }
 }
 
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
@@ -804,24 +809,20 @@ static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream)
 hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, const float* w13s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
-                        float* a_buf, uint8_t* aq, float* as, hipStream_t stream) {
+                        uint8_t* aq, float* as, hipStream_t stream) {
   GemmArgs a{};
   a.eoff = eoff; a.E = E;
   a.act = xq; a.act_scale = xs; a.w = w13; a.w_scale = w13s;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
-  a.aq_out = aq; a.as_out = as; a.a_out = a_buf;
+  a.aq_out = aq; a.as_out = as;
   a.K = H; a.N = 2 * I; a.I = I; a.H = H; a.P = P; a.top_k = top_k;
   a.nblk = nblk;
+  a.n_tiles = I / 128;
   if (BM == 128) {
     a.split = 1;
-    a.n_tiles = I / 64;
     hipLaunchKernelGGL(moe_gemm1_pf_kernel, dim3((unsigned)(nblk * a.n_tiles)), dim3(512), 0, stream, a);
-    const long long slots = (long long)nblk * BM * (I / 4);
-    hipLaunchKernelGGL(requant_rows_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
-                       stream, (const float4*)a_buf, ntpp, I, (uint32_t*)aq, as);
     return hipGetLastError();
   }
-  a.n_tiles = I / 128;
   const int rm = BM < 32 ? BM : 32;
   const int split = BM / rm;
   a.split = split;

@@ -18,7 +18,7 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
 hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, const float* w13s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
-                        float* a_buf, uint8_t* aq, float* as, hipStream_t stream);
+                        uint8_t* aq, float* as, hipStream_t stream);
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, const float* topk_w, int H, int I, int P, int BM,

@@ -52,7 +52,6 @@ void make_layout(int T, int H, int I, int E, int top_k, Layout& L) {
   sz[MOE_TAP_NTPP] = 4;
   sz[MOE_TAP_XQ] = (size_t)T * H;
   sz[MOE_TAP_XS] = (size_t)T * (H / 128) * 4;
-  sz[MOE_TAP_A] = L.BM == 128 ? L.cap * I * 4 : 0;
   sz[MOE_TAP_AQ] = L.cap * I;
   sz[MOE_TAP_AS] = L.cap * (I / 128) * 4;
   sz[MOE_TAP_Y] = P * H * 2;
@@ -147,7 +146,6 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
   int32_t* ntpp = (int32_t*)(ws + L.off[MOE_TAP_NTPP]);
   uint8_t* xq = (uint8_t*)(ws + L.off[MOE_TAP_XQ]);
   float* xs = (float*)(ws + L.off[MOE_TAP_XS]);
-  float* abuf = (float*)(ws + L.off[MOE_TAP_A]);
   uint8_t* aq = (uint8_t*)(ws + L.off[MOE_TAP_AQ]);
   float* as = (float*)(ws + L.off[MOE_TAP_AS]);
   uint16_t* y = (uint16_t*)(ws + L.off[MOE_TAP_Y]);
@@ -168,7 +166,7 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
   if (mark(3)) return MOE_ERR_HIP;
   const int32_t* eoff = moe::align_expert_offsets(scratch, P, E);
   if ((err = moe::launch_gemm1(xq, xs, w13, w13_scale, sorted, eids, ntpp, eoff, E, H, I, P,
-                               top_k, L.BM, nblk, abuf, aq, as, stream)))
+                               top_k, L.BM, nblk, aq, as, stream)))
     return MOE_ERR_HIP;
   if (mark(4)) return MOE_ERR_HIP;
   if ((err = moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, E, tw, H, I, P,

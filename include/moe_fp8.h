@@ -75,7 +75,6 @@ enum {
   MOE_TAP_NTPP,             /* int32 [1] number of sorted rows after padding */
   MOE_TAP_XQ,               /* uint8 [T, H] e4m3fn codes of x */
   MOE_TAP_XS,               /* float32 [T, H/128] scales of x */
-  MOE_TAP_A,                /* float32 [cap, I] silu(gate)*up, sorted order (128-row blocks only) */
   MOE_TAP_AQ,               /* uint8 [cap, I] requantised activation, sorted order */
   MOE_TAP_AS,               /* float32 [cap, I/128] its scales */
   MOE_TAP_Y,                /* bf16 [T*top_k, H] weighted expert output per pair */
