@@ -16,6 +16,7 @@ Prints one JSON line.  value = tokens per second over the step.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,19 @@ MFMA_F16_PEAK = 2.5e15     # dense f16 / bf16 FLOP/s
 # e4m3 operands, GEMM2 on FP8 MFMAs
 STAGE_PEAK = {"gemm1": MFMA_F16_PEAK, "gemm2": MFMA_FP8_PEAK}
 
+# HBM bytes per launch of the two GEMMs, from rocprofv3 FETCH_SIZE (x2) and
+# WRITE_SIZE (x1) passes, each scaled by what the same counter reads for a
+# plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
+# kernel source they were taken on: bench reports null traffic once
+# gemm.hip differs from this hash.
+TRAFFIC_SOURCE_SHA256 = "d69e8d3a5a1471a13e362ec93553957a19be853fc13a05e4cdc000da67f791c1"
+TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
+    "prefill.gemm1": (8867241771, 182000277),
+    "prefill.gemm2": (4491585323, 939644640),
+    "decode.gemm1": (4795742592, 5725931),
+    "decode.gemm2": (2408366336, 7340085),
+}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -39,7 +53,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="dsv3", choices=["dsv3", "mixtral", "qwen3", "tiny"])
-    p.add_argument("--cpu-sample-tokens", type=int, default=12)
+    p.add_argument("--cpu-sample-tokens", type=int, default=16)
     p.add_argument("--phase", default="both", choices=["both", "decode", "prefill"],
                    help="time one batch size only (for per-kernel profiles)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -232,7 +246,13 @@ def main():
     dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
     dom = kernels[dom_name]
     roof = roofline_of(dom["bytes"], dom["flops"], dom["ms"] * 1e-3, dom["peak"])
-    roof.update({"kernel": dom_name, "traffic": None,
+    traffic = None
+    src = os.path.join(ROOT, "fp8_block_quantized_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as fh:
+        same_source = hashlib.sha256(fh.read()).hexdigest() == TRAFFIC_SOURCE_SHA256
+    if args.workload == "dsv3" and same_source and dom_name in TRAFFIC:
+        traffic = float(sum(TRAFFIC[dom_name]))
+    roof.update({"kernel": dom_name, "traffic": traffic, "traffic_unit": "bytes per launch",
                  "alg_bytes_per_launch": dom["bytes"], "alg_flops_per_launch": dom["flops"],
                  "ms_per_launch": dom["ms"]})
 
