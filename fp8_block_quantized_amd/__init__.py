@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_fp8.so")
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIAS"}
-TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "xq", "xs", "aq",
-        "as", "y", "align_scratch"]
+TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "pair_pos", "xq", "xs",
+        "aq", "as", "y", "align_scratch"]
 MAX_EXPERTS = 512
 MAX_TOKENS = 16384
 MAX_TOP_K = 32
@@ -171,11 +171,12 @@ def workspace_taps(workspace, T, H, I, E, top_k):
         "sorted_ids": view("sorted_ids", torch.int32, (cap,)),
         "expert_ids": view("expert_ids", torch.int32, (cap // bm,)),
         "ntpp": view("ntpp", torch.int32, (1,)),
+        "pair_pos": view("pair_pos", torch.int32, (P,)),
         "xq": view("xq", torch.uint8, (T, H)),
         "xs": view("xs", torch.float32, (T, H // 128)),
         "aq": view("aq", torch.uint8, (cap, I)),
         "as": view("as", torch.float32, (cap, I // 128)),
-        "y": view("y", torch.bfloat16, (P, H)),
+        "y": view("y", torch.bfloat16, (cap, -(-H // 256) * 256)),
     }
 
 

@@ -14,7 +14,8 @@
 //               expert table, the sentinels and the padded total.
 //   3. scatter: each chunk ranks its pairs stably inside their expert (a
 //               ballot match inside each wave plus per-wave counts in LDS)
-//               and writes them to base + rank.
+//               and writes them to base + rank; the forward also keeps the
+//               inverse map (pair -> sorted row) for the combine.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
 
 __global__ __launch_bounds__(1024) void align_scatter_kernel(
     const int32_t* __restrict__ ids, int P, int E, int ebits, const int32_t* __restrict__ base,
-    int32_t* __restrict__ sorted_ids) {
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ pair_pos) {
   __shared__ int wcnt[kChunk / 64][kMaxE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < (kChunk / 64) * E; i += kChunk) wcnt[i / E][i % E] = 0;
@@ -107,7 +108,9 @@ __global__ __launch_bounds__(1024) void align_scatter_kernel(
   if (valid) {
     int before = 0;
     for (int w = 0; w < wave; ++w) before += wcnt[w][e];
-    sorted_ids[base[(size_t)blockIdx.x * E + e] + before + rank_in_wave] = p;
+    const int pos = base[(size_t)blockIdx.x * E + e] + before + rank_in_wave;
+    sorted_ids[pos] = p;
+    if (pair_pos) pair_pos[p] = pos;
   }
 }
 
@@ -124,7 +127,8 @@ const int32_t* align_expert_offsets(const void* scratch, int P, int E) {
 }
 
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
-                        int32_t* expert_ids, int32_t* ntpp, void* scratch, hipStream_t stream) {
+                        int32_t* expert_ids, int32_t* ntpp, int32_t* pair_pos, void* scratch,
+                        hipStream_t stream) {
   const int nchunk = (P + kChunk - 1) / kChunk;
   int32_t* counts = (int32_t*)scratch;
   int32_t* base = counts + (size_t)nchunk * E;
@@ -137,7 +141,7 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
                      base, sorted_ids, expert_ids, ntpp, eoff);
   if (nchunk > 0)
     hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, P, E, ebits,
-                       base, sorted_ids);
+                       base, sorted_ids, pair_pos);
   return hipGetLastError();
 }
 

@@ -48,10 +48,9 @@ struct GemmArgs {
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* ntpp;
-  const float* topk_w;       // GEMM2: [P]
   uint8_t* aq_out;           // GEMM1: [cap, I]
   float* as_out;             // GEMM1: [cap, I/128]
-  uint16_t* y_out;           // GEMM2: bf16 [P, H]
+  uint16_t* y_out;           // GEMM2: bf16 [cap, y_stride], sorted rows, before the routing weight
   int K;                     // reduction length (H or I)
   int N;                     // weight rows per expert (2I or H)
   int I;
@@ -63,6 +62,7 @@ struct GemmArgs {
   const int32_t* eoff;       // [E + 1] first block of each expert, blocks in use
   int E;
   int split;                 // workgroups per row block (BM / rows per workgroup)
+  int y_stride;              // GEMM2: row stride of y_out (H rounded up to 256)
 };
 
 // M0 is written only inside these statements, each right before its load;
@@ -71,6 +71,16 @@ struct GemmArgs {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+// The same loads with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset (the saddr form): no 64-bit address arithmetic per lane.
+__device__ __forceinline__ void dma16s(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
@@ -251,21 +261,20 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
     sw0 = sw0_n;
   }
 
-  // y[p] = routing weight * acc, bf16, in pair order (real rows only)
+  // y of each sorted row of a real pair, bf16 (the combine applies the
+  // routing weight)
   if (!wave_on) return;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int rq = 16 * q + l16;
-    const int p = args.sorted_ids[row0 + rq];
-    if (p >= args.P) continue;
-    const float wt = args.topk_w[p];
-    uint16_t* yrow = args.y_out + (size_t)p * args.H;
+    if (args.sorted_ids[row0 + rq] >= args.P) continue;
+    uint16_t* yrow = args.y_out + (size_t)(row0 + rq) * args.y_stride;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
       const int h0 = 256 * j + 64 * wave + 16 * pp + 4 * g;
       uint2 v;
-      v.x = f32_to_bf16_bits(acc[pp][q][0] * wt) | (f32_to_bf16_bits(acc[pp][q][1] * wt) << 16);
-      v.y = f32_to_bf16_bits(acc[pp][q][2] * wt) | (f32_to_bf16_bits(acc[pp][q][3] * wt) << 16);
+      v.x = f32_to_bf16_bits(acc[pp][q][0]) | (f32_to_bf16_bits(acc[pp][q][1]) << 16);
+      v.y = f32_to_bf16_bits(acc[pp][q][2]) | (f32_to_bf16_bits(acc[pp][q][3]) << 16);
       *(uint2*)(yrow + h0) = v;
     }
   }
@@ -500,11 +509,46 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
 constexpr int kRingStages = 3;
 constexpr int kRingW = 256 * 128;      // 256 weight rows x one 128-byte K block
 
-// GEMM2 prefill: 128 sorted rows x 256 output features per workgroup, eight
-// waves (two per SIMD, so one wave's scale FMAs overlap the other's MFMAs);
-// wave w owns tokens [64 (w>>2), +64) x features [64 (w&3), +64).
+// GEMM2 prefill, persistent.  A tile is 128 sorted rows x 256 output
+// features; eight waves (two per SIMD) own 64 tokens x 64 features each, with
+// one FP8 MFMA per 16x16 tile and K block and a float32 accumulator.
+//
+// The grid is one workgroup per CU.  Each XCD takes a contiguous range of the
+// tiles in use (expert-major order, so an expert's weight panel is read by
+// row blocks running together on one XCD), and the XCD's workgroups walk it
+// with a stride of their count.  A workgroup's tiles form one stream of
+// K-block stages through a three-stage LDS ring: the first stages of the next
+// tile load while the current tile finishes and stores its outputs, so no
+// tile waits for its first operands and no workgroup start-up is exposed.
+//
+// Every wait is a hand-placed vmcnt: before computing stage s, the loads of
+// stage s + 1 and the 16 output stores of a tile that ended one or two steps
+// earlier may still be in flight (vector memory operations retire in order).
+// The epilogue therefore stores unconditionally (the output has whole
+// 256-feature tiles per row, padding rows included) and issues no loads.
+// Needs at least two K blocks per tile.
 constexpr int kPf2Loads = 7;               // DMA instructions per wave per stage
+constexpr int kPf2Stores = 16;             // output stores per wave per tile
 constexpr int kPf2S = 2048;                // token scales, eight 256-byte wave slots
+
+struct TileId {
+  int e, b, j;
+};
+
+// Logical tile L -> (expert, m block, n tile) in expert-major order, by a
+// binary search over the expert block offsets.  Scalar loads only: they stay
+// out of the vector memory counter that the ring's waits rely on.
+__device__ __forceinline__ TileId tile_id(int L, const GemmArgs& a) {
+  const int nt = a.n_tiles;
+  int lo = 0, hi = a.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (load_uniform(a.eoff + mid) * nt <= L) lo = mid; else hi = mid - 1;
+  }
+  const int b0 = load_uniform(a.eoff + lo), nb = load_uniform(a.eoff + lo + 1) - b0;
+  const int local = L - b0 * nt, j = local / nb;
+  return {lo, b0 + (local - j * nb), j};
+}
 
 __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   constexpr int BM = 128;
@@ -514,102 +558,127 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wave >> 2, wf = wave & 3;
   const int g = lane >> 4, l16 = lane & 15;
-  const TileCoord tc = tile_of(blockIdx.x, args);
-  if (!tc.valid) return;
-  const int b = tc.b, j = tc.j;
-  const int e = load_uniform(args.expert_ids + b);
-  const int K = args.K, nkb = K >> 7;
-  const int row0 = b * BM, n0 = 256 * j;
+  const int K = args.K, nkb = K >> 7, N = args.N;
 
-  const uint8_t* wsrc[4];
+  // this workgroup's tiles
+  const int n_real = load_uniform(args.eoff + args.E) * args.n_tiles;
+  const int per_xcd = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int q8 = n_real >> 3, r8 = n_real & 7;
+  const int xbeg = xcd * q8 + (xcd < r8 ? xcd : r8), xcnt = q8 + (xcd < r8 ? 1 : 0);
+  const int ntile = slot < xcnt ? (xcnt - 1 - slot) / per_xcd + 1 : 0;
+  if (ntile == 0) return;
+  const int G = ntile * nkb;
+  auto tile_at = [&](int i) { return tile_id(xbeg + slot + i * per_xcd, args); };
+
+  // this lane's 16-byte pieces of a stage: weight rows (wave*4 + i)*8 + lr of
+  // the tile's 256, token rows (wave*2 + i)*8 + lr of its 128, chunk lc under
+  // the rows' XOR swizzle (rows 8 apart share it)
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+  auto w_offsets = [&](int j, uint32_t (&o)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
-    const int row = n0 + r < args.N ? n0 + r : 0;    // rows past H: any valid row, never stored
-    wsrc[i] = args.w + ((size_t)e * args.N + row) * K + lc * 16;
-  }
-  const uint8_t* asrc[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int pos = (wave * 2 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
-    asrc[i] = args.act + (size_t)(row0 + r) * K + lc * 16;
-  }
-  const float* ssrc = args.act_scale + (size_t)(row0 + (wave & 1) * 64 + lane) * nkb;
-  auto issue = [&](int stage, int kb) {
-    const uint32_t base = lds_offset(ring + stage * kStage);
-    const size_t ko = (size_t)kb * 128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + ko, base + (wave * 4 + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(asrc[i] + ko, base + kRingW + (wave * 2 + i) * 1024);
-    dma4(ssrc + kb, base + kRingW + kA + wave * 256);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 256 * j + (wave * 4 + i) * 8 + lr;
+      o[i] = (uint32_t)((row < N ? row : 0) * K + lc * 16);    // rows past H: any valid row
+    }
   };
-  const int nf = n0 + 64 * wf;
-  const float* wsp = args.w_scale + ((size_t)e * (args.N >> 7) + ((nf < args.N ? nf : 0) >> 7)) * nkb;
-  int poff[4][2], qoff[4][2];
+  uint32_t aoff[2];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    const int r = 64 * wf + 16 * pp + l16;
-    poff[pp][0] = r * 128 + ((g ^ (r & 7)) << 4);
-    poff[pp][1] = r * 128 + (((g + 4) ^ (r & 7)) << 4);
+  for (int i = 0; i < 2; ++i) aoff[i] = (uint32_t)(((wave * 2 + i) * 8 + lr) * K + lc * 16);
+  const uint32_t soff = (uint32_t)(((wave & 1) * 64 + lane) * nkb * 4);
+  auto issue = [&](int stage, const TileId& t, const uint32_t (&wo)[4], int kb) {
+    const uint32_t base = lds_offset(ring + stage * kStage);
+    const uint8_t* wb = args.w + (size_t)t.e * N * K + (size_t)kb * 128;
+    const uint8_t* ab = args.act + (size_t)t.b * BM * K + (size_t)kb * 128;
+    const uint8_t* sb = (const uint8_t*)(args.act_scale + (size_t)t.b * BM * nkb + kb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16s(wo[i], wb, base + (wave * 4 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16s(aoff[i], ab, base + kRingW + (wave * 2 + i) * 1024);
+    dma4s(soff, sb, base + kRingW + kA + wave * 256);
+  };
+  // LDS byte offsets of this lane's operand pieces: row, chunks g and g + 4;
+  // rows 16 apart share the swizzle, so each fragment is a base + immediate
+  int pbase[2], qbase[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    pbase[h] = (64 * wf + l16) * 128 + (((g + 4 * h) ^ (l16 & 7)) << 4);
+    qbase[h] = kRingW + (64 * wt + l16) * 128 + (((g + 4 * h) ^ (l16 & 7)) << 4);
   }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 64 * wt + 16 * q + l16;
-    qoff[q][0] = kRingW + r * 128 + ((g ^ (r & 7)) << 4);
-    qoff[q][1] = kRingW + r * 128 + (((g + 4) ^ (r & 7)) << 4);
-  }
-  v4f acc[4][4];
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  if (nkb > 1) issue(1, 1);
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) wait_vmem<kPf2Loads>(); else wait_vmem<0>();
-    barrier_raw();
-    if (kb + 2 < nkb) issue((kb + 2) % kRingStages, kb + 2);
-    const uint8_t* st = ring + (kb % kRingStages) * kStage;
-    const float sw = load_uniform(wsp + kb);
-    v8i pf[4];
+  TileId cur = tile_at(0), nxt = cur;
+  uint32_t cwo[4], nwo[4];
+  w_offsets(cur.j, cwo);
+  if (ntile > 1) {
+    nxt = tile_at(1);
+    w_offsets(nxt.j, nwo);
+  }
+  issue(0, cur, cwo, 0);
+  issue(1, cur, cwo, 1);
+  int s = 0;
+  for (int ti = 0; ti < ntile; ++ti) {
+    const int nf = 256 * cur.j + 64 * wf;
+    const float* wsp = args.w_scale + ((size_t)cur.e * (N >> 7) + ((nf < N ? nf : 0) >> 7)) * nkb;
+    v4f acc[4][4];
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const uint4 a0 = *(const uint4*)(st + poff[pp][0]);
-      const uint4 a1 = *(const uint4*)(st + poff[pp][1]);
-      pf[pp] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-    }
+    for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 b0 = *(const uint4*)(st + qoff[q][0]);
-      const uint4 b1 = *(const uint4*)(st + qoff[q][1]);
-      const v8i bq = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-      const float sc = *(const float*)(st + kRingW + kA + (64 * wt + 16 * q + l16) * 4) * sw;
+      for (int q = 0; q < 4; ++q) acc[pp][q] = zero;
+    for (int kb = 0; kb < nkb; ++kb, ++s) {
+      const bool more = s + 1 < G, stores = ti > 0 && kb < 2;
+      if (more) {
+        if (stores) wait_vmem<kPf2Loads + kPf2Stores>(); else wait_vmem<kPf2Loads>();
+      } else {
+        if (stores) wait_vmem<kPf2Stores>(); else wait_vmem<0>();
+      }
+      barrier_raw();
+      if (s + 2 < G) {
+        if (kb + 2 < nkb) issue((s + 2) % kRingStages, cur, cwo, kb + 2);
+        else issue((s + 2) % kRingStages, nxt, nwo, kb + 2 - nkb);
+      }
+      const uint8_t* st = ring + (s % kRingStages) * kStage;
+      const float sw = load_uniform(wsp + kb);
+      v8i pf[4];
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf[pp], bq, zero, 0, 0, 0, 0, 0, 0);
+        const uint4 a0 = *(const uint4*)(st + pbase[0] + pp * 2048);
+        const uint4 a1 = *(const uint4*)(st + pbase[1] + pp * 2048);
+        pf[pp] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 b0 = *(const uint4*)(st + qbase[0] + q * 2048);
+        const uint4 b1 = *(const uint4*)(st + qbase[1] + q * 2048);
+        const v8i bq = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        const float sc = *(const float*)(st + kRingW + kA + (64 * wt + 16 * q + l16) * 4) * sw;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf[pp], bq, zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
+        }
       }
     }
-  }
-  // y[p] = routing weight * acc, bf16, in pair order (real rows only)
+    // y rows of the tile, bf16, every row and feature (kPf2Stores stores)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int p = args.sorted_ids[row0 + 64 * wt + 16 * q + l16];
-    if (p >= args.P) continue;
-    const float wt_p = args.topk_w[p];
-    uint16_t* yrow = args.y_out + (size_t)p * args.H;
+    for (int q = 0; q < 4; ++q) {
+      uint16_t* yrow = args.y_out + (size_t)(cur.b * BM + 64 * wt + 16 * q + l16) * args.y_stride + nf + 4 * g;
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int h0 = nf + 16 * pp + 4 * g;
-      if (h0 >= args.H) continue;
-      uint2 v;
-      v.x = f32_to_bf16_bits(acc[pp][q][0] * wt_p) | (f32_to_bf16_bits(acc[pp][q][1] * wt_p) << 16);
-      v.y = f32_to_bf16_bits(acc[pp][q][2] * wt_p) | (f32_to_bf16_bits(acc[pp][q][3] * wt_p) << 16);
-      *(uint2*)(yrow + h0) = v;
+      for (int pp = 0; pp < 4; ++pp) {
+        uint2 v;
+        v.x = f32_to_bf16_bits(acc[pp][q][0]) | (f32_to_bf16_bits(acc[pp][q][1]) << 16);
+        v.y = f32_to_bf16_bits(acc[pp][q][2]) | (f32_to_bf16_bits(acc[pp][q][3]) << 16);
+        *(uint2*)(yrow + 16 * pp) = v;
+      }
+    }
+    if (ti + 1 < ntile) {
+      cur = nxt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cwo[i] = nwo[i];
+      if (ti + 2 < ntile) {
+        nxt = tile_at(ti + 2);
+        w_offsets(nxt.j, nwo);
+      }
     }
   }
 }
@@ -792,8 +861,17 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
 
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
-  if (BM == 128) {
-    hipLaunchKernelGGL(moe_gemm2_pf_kernel, grid, dim3(512), 0, stream, a);
+  if (BM == 128 && a.K >= 256) {
+    // one persistent workgroup per CU, a multiple of the 8 XCDs
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    const long long tiles = (long long)a.nblk * a.n_tiles;
+    long long wg = cus / 8 * 8;
+    if (wg > (tiles + 7) / 8 * 8) wg = (tiles + 7) / 8 * 8;
+    if (wg < 8) wg = 8;
+    hipLaunchKernelGGL(moe_gemm2_pf_kernel, dim3((unsigned)wg), dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   switch (BM) {
@@ -838,13 +916,13 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
 
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
-                        const int32_t* eoff, int E, const float* topk_w, int H, int I, int P, int BM,
-                        int nblk, uint16_t* y, hipStream_t stream) {
+                        const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
+                        uint16_t* y, int y_stride, hipStream_t stream) {
   GemmArgs a{};
   a.eoff = eoff; a.E = E; a.split = 1;
   a.act = aq; a.act_scale = as; a.w = w2; a.w_scale = w2s;
-  a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp; a.topk_w = topk_w;
-  a.y_out = y;
+  a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
+  a.y_out = y; a.y_stride = y_stride;
   a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
   a.n_tiles = (H + 255) / 256; a.nblk = nblk;
   return launch_gemm2_bm(a, BM, stream);

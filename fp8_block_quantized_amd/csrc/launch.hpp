@@ -14,16 +14,18 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int top_k, int
 size_t align_scratch_bytes(int P, int E);
 const int32_t* align_expert_offsets(const void* scratch, int P, int E);
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
-                        int32_t* expert_ids, int32_t* ntpp, void* scratch, hipStream_t stream);
+                        int32_t* expert_ids, int32_t* ntpp, int32_t* pair_pos, void* scratch,
+                        hipStream_t stream);
 hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, const float* w13s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
                         uint8_t* aq, float* as, hipStream_t stream);
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
-                        const int32_t* eoff, int E, const float* topk_w, int H, int I, int P, int BM,
-                        int nblk, uint16_t* y, hipStream_t stream);
-hipError_t launch_combine(const uint16_t* y, int T, int H, int top_k, uint16_t* out,
+                        const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
+                        uint16_t* y, int y_stride, hipStream_t stream);
+hipError_t launch_combine(const uint16_t* y, int y_stride, const int32_t* pair_pos,
+                          const float* topk_w, int T, int H, int top_k, uint16_t* out,
                           hipStream_t stream);
 
 }  // namespace moe

@@ -12,6 +12,9 @@ namespace {
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+// row stride of the per-pair outputs: whole 256-feature tiles, so that the
+// GEMM2 epilogue stores unconditionally
+size_t y_stride(int H) { return round_up((size_t)H, 256); }
 
 int check_moe_shape(int T, int H, int I, int E, int top_k) {
   if (T < 1 || T > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
@@ -50,11 +53,12 @@ void make_layout(int T, int H, int I, int E, int top_k, Layout& L) {
   sz[MOE_TAP_SORTED_IDS] = L.cap * 4;
   sz[MOE_TAP_EXPERT_IDS] = (L.cap / L.BM) * 4;
   sz[MOE_TAP_NTPP] = 4;
+  sz[MOE_TAP_PAIR_POS] = P * 4;
   sz[MOE_TAP_XQ] = (size_t)T * H;
   sz[MOE_TAP_XS] = (size_t)T * (H / 128) * 4;
   sz[MOE_TAP_AQ] = L.cap * I;
   sz[MOE_TAP_AS] = L.cap * (I / 128) * 4;
-  sz[MOE_TAP_Y] = P * H * 2;
+  sz[MOE_TAP_Y] = L.cap * y_stride(H) * 2;
   sz[MOE_TAP_ALIGN_SCRATCH] = moe::align_scratch_bytes((int)P, E);
   size_t o = 0;
   for (int i = 0; i < MOE_TAP_COUNT; ++i) {
@@ -149,6 +153,7 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
   uint8_t* aq = (uint8_t*)(ws + L.off[MOE_TAP_AQ]);
   float* as = (float*)(ws + L.off[MOE_TAP_AS]);
   uint16_t* y = (uint16_t*)(ws + L.off[MOE_TAP_Y]);
+  int32_t* ppos = (int32_t*)(ws + L.off[MOE_TAP_PAIR_POS]);
   void* scratch = ws + L.off[MOE_TAP_ALIGN_SCRATCH];
   const int P = T * top_k;
   const int nblk = (int)(L.cap / L.BM);
@@ -159,7 +164,7 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
   if ((err = moe::launch_topk_softmax(router_logits, T, E, top_k, renormalize, ids, tw, stream)))
     return MOE_ERR_HIP;
   if (mark(1)) return MOE_ERR_HIP;
-  if ((err = moe::launch_align(ids, P, E, L.BM, sorted, eids, ntpp, scratch, stream)))
+  if ((err = moe::launch_align(ids, P, E, L.BM, sorted, eids, ntpp, ppos, scratch, stream)))
     return MOE_ERR_HIP;
   if (mark(2)) return MOE_ERR_HIP;
   if ((err = moe::launch_group_quant(x, T, H, xq, xs, stream))) return MOE_ERR_HIP;
@@ -169,11 +174,12 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
                                top_k, L.BM, nblk, aq, as, stream)))
     return MOE_ERR_HIP;
   if (mark(4)) return MOE_ERR_HIP;
-  if ((err = moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, E, tw, H, I, P,
-                               L.BM, nblk, y, stream)))
+  if ((err = moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, P, L.BM,
+                               nblk, y, (int)y_stride(H), stream)))
     return MOE_ERR_HIP;
   if (mark(5)) return MOE_ERR_HIP;
-  if ((err = moe::launch_combine(y, T, H, top_k, (uint16_t*)out, stream))) return MOE_ERR_HIP;
+  if ((err = moe::launch_combine(y, (int)y_stride(H), ppos, tw, T, H, top_k, (uint16_t*)out, stream)))
+    return MOE_ERR_HIP;
   if (mark(6)) return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -244,7 +250,7 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m, int
   if (scratch_bytes < moe::align_scratch_bytes(P, E) || ((uintptr_t)scratch % 4))
     return MOE_ERR_WORKSPACE;
   return moe::launch_align(topk_ids, P, E, block_m, sorted_ids, expert_ids, num_tokens_post_padded,
-                           scratch, stream)
+                           nullptr, scratch, stream)
              ? MOE_ERR_HIP
              : MOE_OK;
 }

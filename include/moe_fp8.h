@@ -73,11 +73,13 @@ enum {
   MOE_TAP_SORTED_IDS,       /* int32 [cap] pair index p = t*top_k + j, sentinel T*top_k */
   MOE_TAP_EXPERT_IDS,       /* int32 [cap / block_m] expert of each block */
   MOE_TAP_NTPP,             /* int32 [1] number of sorted rows after padding */
+  MOE_TAP_PAIR_POS,         /* int32 [T*top_k] sorted row of each pair (inverse of sorted_ids) */
   MOE_TAP_XQ,               /* uint8 [T, H] e4m3fn codes of x */
   MOE_TAP_XS,               /* float32 [T, H/128] scales of x */
   MOE_TAP_AQ,               /* uint8 [cap, I] requantised activation, sorted order */
   MOE_TAP_AS,               /* float32 [cap, I/128] its scales */
-  MOE_TAP_Y,                /* bf16 [T*top_k, H] weighted expert output per pair */
+  MOE_TAP_Y,                /* bf16 [cap, roundup(H, 256)] expert output per sorted row, before
+                               the routing weight (rows of padding undefined) */
   MOE_TAP_ALIGN_SCRATCH,    /* int32 scratch of the sort-and-pad stage */
   MOE_TAP_COUNT
 };

@@ -75,8 +75,8 @@ def test_workspace_layout_is_disjoint_and_aligned():
         P = T * k
         cap = -(-(P + E * (bm - 1)) // bm) * bm
         size = {"topk_ids": 4 * P, "topk_weights": 4 * P, "sorted_ids": 4 * cap,
-                "expert_ids": 4 * (cap // bm), "ntpp": 4, "xq": T * H, "xs": 4 * T * H // 128,
-                "aq": cap * I, "as": 4 * cap * I // 128, "y": 2 * P * H, "align_scratch": 0}
+                "expert_ids": 4 * (cap // bm), "ntpp": 4, "pair_pos": 4 * P, "xq": T * H, "xs": 4 * T * H // 128,
+                "aq": cap * I, "as": 4 * cap * I // 128, "y": 2 * cap * (-(-H // 256) * 256), "align_scratch": 0}
         names = moe.TAPS
         for a, b in zip(names, names[1:]):
             assert off[a] % 256 == 0
