@@ -38,12 +38,12 @@ STAGE_PEAK = {"gemm1": MFMA_F16_PEAK, "gemm2": MFMA_FP8_PEAK}
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
 # kernel source they were taken on: bench reports null traffic once
 # gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "d69e8d3a5a1471a13e362ec93553957a19be853fc13a05e4cdc000da67f791c1"
+TRAFFIC_SOURCE_SHA256 = "6d7a0b8cec67f9becd8fb3ec5779182a3c8198d2e5ce0a0166ed37f1803c81db"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
-    "prefill.gemm1": (8867241771, 182000277),
-    "prefill.gemm2": (4491585323, 939644640),
-    "decode.gemm1": (4795742592, 5725931),
-    "decode.gemm2": (2408366336, 7340085),
+    "prefill.gemm1": (8866457685, 181931029),
+    "prefill.gemm2": (4463134208, 1207437835),
+    "decode.gemm1": (4796014592, 5720363),
+    "decode.gemm2": (2408647893, 7340373),
 }
 
 
@@ -87,8 +87,8 @@ def algorithmic(ids, T, H, I, E, k):
             "align": (8 * P, 0),
             "quant": (2 * T * H + T * H + 4 * T * (H // 128), 0),
             "gemm1": (w13_b + T * H + 4 * T * (H // 128) + a_b, 4 * P * H * I),
-            "gemm2": (w2_b + a_b + 4 * P + 2 * P * H, 2 * P * H * I),
-            "combine": (2 * P * H + 2 * T * H, 0),
+            "gemm2": (w2_b + a_b + 2 * P * H, 2 * P * H * I),
+            "combine": (2 * P * H + 8 * P + 2 * T * H, 0),
         },
     }
 
