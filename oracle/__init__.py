@@ -20,6 +20,8 @@ Sources (the vLLM pages on quantization and MoE optimisations):
     ``make_fp8_moe_quant_config`` (block_shape, per-token activation
     scales) and the quant keys for dynamic 128-group activations with
     static 128-block weights, symmetric.
+  * overview page, "W8A8BlockFp8LinearOp - Block FP8 GEMM Dispatch": the
+    dense block-FP8 GEMM of DeepSeek-V3-style layers.
   * "vllm.model_executor.layers.quantization.online.nvfp4" API page,
     ``_quantize_moe_weight_to_nvfp4``: stacked (E, N, K) expert weights, an
     amax clamped below at 1e-8, scales stored as dequant multipliers.
@@ -31,6 +33,8 @@ Modules:
   align   sort-and-pad of (token, slot) pairs by expert (moe_align).
   moe     the whole layer: quant -> GEMM1 -> SiLU*mul -> requant -> GEMM2 ->
           weighted combine, with weights dequantised to float64.
+  linear  the dense block-FP8 linear layer (the E = 1 neighbour of the layer's
+          second GEMM): quant -> block-scaled product -> bf16.
 
 Parity status of each function is stated in its docstring; every function
 here is pinned by a test in ``tests/test_oracle_*.py``.

@@ -36,6 +36,9 @@ MOE_WORKLOADS = {
                   T=(1, 32, 4096), logits="normal"),
 }
 QUANT_WORKLOAD = dict(index=4, M=16384, K=7168, outlier_frac=0.01, outlier_mul=100.0)
+# Dense block-FP8 linear: a DeepSeek-V3-shaped dense down projection
+# (out features 7168, in features 18432) at a decode and a prefill batch
+LINEAR_WORKLOAD = dict(index=5, N=7168, K=18432, M=(64, 8192))
 
 WEIGHT_STD = 0.02
 BLOCK = 128
@@ -120,3 +123,17 @@ def quant_input(M=None, K=None, device="cpu", seed_base=None,
     mask = torch.rand((M, K), generator=_gen(device, seed_base + 3), device=device) < frac
     x = torch.where(mask, x * mul, x)
     return x.to(torch.bfloat16).contiguous()
+
+
+def make_linear(M, N, K, seed_base, device="cpu", std=WEIGHT_STD):
+    """Dense linear inputs: x bf16 [M, K] ~ N(0, 1) (seed_base + 0) and a
+    weight [N, K] ~ N(0, std) (seed_base + 2), block-quantised to e4m3fn codes
+    [N, K] with float32 scales [N/128, K/128]."""
+    if N % BLOCK or K % BLOCK:
+        raise ValueError("N and K must be multiples of 128")
+    x = torch.randn((M, K), generator=_gen(device, seed_base + 0), device=device,
+                    dtype=torch.float32).to(torch.bfloat16).contiguous()
+    w = torch.randn((N, K), generator=_gen(device, seed_base + 2), device=device,
+                    dtype=torch.float32) * std
+    wq, ws = block_quantize_e4m3(w)
+    return x, wq, ws
