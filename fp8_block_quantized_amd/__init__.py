@@ -28,7 +28,8 @@ STAGES = ["router", "align", "quant", "gemm1", "gemm2", "combine"]
 
 EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layout",
            "moe_fp8_forward", "moe_fp8_forward_traced", "per_token_group_quant_fp8", "moe_topk_softmax",
-           "moe_align_scratch_bytes", "moe_align", "moe_status_string"]
+           "moe_align_scratch_bytes", "moe_align", "moe_status_string",
+           "fp8_block_linear_workspace_bytes", "fp8_block_linear"]
 
 
 class MoeError(RuntimeError):
@@ -68,6 +69,10 @@ def load_library(path=LIB_PATH):
     lib.moe_align_scratch_bytes.restype = c_size
     lib.moe_align.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]
     lib.moe_align.restype = c_int
+    lib.fp8_block_linear_workspace_bytes.argtypes = [c_int] * 3
+    lib.fp8_block_linear_workspace_bytes.restype = c_size
+    lib.fp8_block_linear.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, vp, c_size, vp]
+    lib.fp8_block_linear.restype = c_int
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -227,3 +232,27 @@ def moe_align(topk_ids, num_experts, block_m, stream=None):
                        _dev(scratch, torch.uint8, "scratch"), scratch.numel(), _stream(stream))
     _check("moe_align", st)
     return sorted_ids, expert_ids, ntpp
+
+
+def fp8_block_linear_workspace_bytes(M, N, K):
+    return load_library().fp8_block_linear_workspace_bytes(M, N, K)
+
+
+def fp8_block_linear(x, w, w_scale, out=None, workspace=None, stream=None):
+    """Dense block-FP8 linear: x bf16 [M, K], w uint8 e4m3fn [N, K], w_scale f32
+    [N/128, K/128] -> out bf16 [M, N] (x quantised per 128-group of each row)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        n = fp8_block_linear_workspace_bytes(M, N, K)
+        if n == 0:
+            raise MoeError("fp8_block_linear_workspace_bytes", -2)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    st = load_library().fp8_block_linear(
+        _dev(x, torch.bfloat16, "x"), _dev(w, torch.uint8, "w"), _dev(w_scale, torch.float32, "w_scale"),
+        M, N, K, _dev(out, torch.bfloat16, "out"), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check("fp8_block_linear", st)
+    return out

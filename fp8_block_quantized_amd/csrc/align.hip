@@ -114,6 +114,33 @@ __global__ __launch_bounds__(1024) void align_scatter_kernel(
   }
 }
 
+// The layout of one expert owning every row (the dense linear): sorted row r
+// holds row r of the input (the sentinel M past its end), every block belongs
+// to expert 0, eoff = {0, nblk} and the padded row count is nblk * BM.
+__global__ __launch_bounds__(256) void identity_layout_kernel(int M, int BM, int nblk,
+                                                              int32_t* __restrict__ sorted_ids,
+                                                              int32_t* __restrict__ expert_ids,
+                                                              int32_t* __restrict__ eoff,
+                                                              int32_t* __restrict__ ntpp) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < nblk * BM) sorted_ids[i] = i < M ? i : M;
+  if (i < nblk) expert_ids[i] = 0;
+  if (i == 0) {
+    eoff[0] = 0;
+    eoff[1] = nblk;
+    ntpp[0] = nblk * BM;
+  }
+}
+
+hipError_t launch_identity_layout(int M, int BM, int nblk, int32_t* sorted_ids,
+                                  int32_t* expert_ids, int32_t* eoff, int32_t* ntpp,
+                                  hipStream_t stream) {
+  const long long n = (long long)nblk * BM;
+  hipLaunchKernelGGL(identity_layout_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     M, BM, nblk, sorted_ids, expert_ids, eoff, ntpp);
+  return hipGetLastError();
+}
+
 // scratch: per-chunk counts and bases [nchunk, E] each, then the expert
 // block offsets [E + 1] that the GEMMs use to order their tiles
 size_t align_scratch_bytes(int P, int E) {

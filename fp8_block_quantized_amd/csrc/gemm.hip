@@ -63,6 +63,8 @@ struct GemmArgs {
   int E;
   int split;                 // workgroups per row block (BM / rows per workgroup)
   int y_stride;              // GEMM2: row stride of y_out (H rounded up to 256)
+  int y_rows, y_cols;        // GEMM2: stored region of y_out; other stores go to y_dump
+  uint16_t* y_dump;          // GEMM2: 512 bytes
 };
 
 // M0 is written only inside these statements, each right before its load;
@@ -659,16 +661,21 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
         }
       }
     }
-    // y rows of the tile, bf16, every row and feature (kPf2Stores stores)
+    // y rows of the tile, bf16: kPf2Stores stores whatever the bounds, the
+    // ones outside the stored region (a dense output's ragged edge) into the dump
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint16_t* yrow = args.y_out + (size_t)(cur.b * BM + 64 * wt + 16 * q + l16) * args.y_stride + nf + 4 * g;
+      const int row = cur.b * BM + 64 * wt + 16 * q + l16;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
+        const int col = nf + 16 * pp + 4 * g;
+        uint16_t* dst = row < args.y_rows && col < args.y_cols
+                            ? args.y_out + (size_t)row * args.y_stride + col
+                            : args.y_dump + 4 * lane;
         uint2 v;
         v.x = f32_to_bf16_bits(acc[pp][q][0]) | (f32_to_bf16_bits(acc[pp][q][1]) << 16);
         v.y = f32_to_bf16_bits(acc[pp][q][2]) | (f32_to_bf16_bits(acc[pp][q][3]) << 16);
-        *(uint2*)(yrow + 16 * pp) = v;
+        *(uint2*)dst = v;
       }
     }
     if (ti + 1 < ntile) {
@@ -923,8 +930,25 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
   a.act = aq; a.act_scale = as; a.w = w2; a.w_scale = w2s;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
   a.y_out = y; a.y_stride = y_stride;
+  a.y_rows = nblk * BM; a.y_cols = y_stride; a.y_dump = y;
   a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
   a.n_tiles = (H + 255) / 256; a.nblk = nblk;
+  return launch_gemm2_bm(a, BM, stream);
+}
+
+hipError_t launch_gemm2_bounded(const uint8_t* act, const float* act_scale, const uint8_t* w,
+                                const float* w_scale, const int32_t* sorted_ids,
+                                const int32_t* expert_ids, const int32_t* ntpp, const int32_t* eoff,
+                                int N, int K, int P, int BM, int nblk, uint16_t* y, int y_stride,
+                                int y_rows, int y_cols, uint16_t* y_dump, hipStream_t stream) {
+  GemmArgs a{};
+  a.eoff = eoff; a.E = 1; a.split = 1;
+  a.act = act; a.act_scale = act_scale; a.w = w; a.w_scale = w_scale;
+  a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
+  a.y_out = y; a.y_stride = y_stride;
+  a.y_rows = y_rows; a.y_cols = y_cols; a.y_dump = y_dump;
+  a.K = K; a.N = N; a.I = K; a.H = N; a.P = P; a.top_k = 1;
+  a.n_tiles = (N + 255) / 256; a.nblk = nblk;
   return launch_gemm2_bm(a, BM, stream);
 }
 

@@ -20,6 +20,7 @@ int check_moe_shape(int T, int H, int I, int E, int top_k) {
   if (T < 1 || T > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
   if (H < 128 || H % 128 || I < 128 || I % 128) return MOE_ERR_SHAPE;
   if (H > (1 << 16) || I > (1 << 16)) return MOE_ERR_SHAPE;
+  if (2LL * I * H >= (1LL << 31)) return MOE_ERR_SHAPE;   // 32-bit offsets inside one expert
   if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
   if (top_k < 1 || top_k > E || top_k > MOE_MAX_TOP_K) return MOE_ERR_SHAPE;
   return MOE_OK;
@@ -71,6 +72,39 @@ void make_layout(int T, int H, int I, int E, int top_k, Layout& L) {
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return na && nb && x < y + nb && y < x + na;
+}
+
+// Dense linear: one expert owning every row, in blocks of BM rows.
+struct LinearLayout {
+  int BM, nblk;
+  size_t cap, xq, xs, sorted, eids, meta, dump, total;
+};
+
+int check_linear_shape(int M, int N, int K) {
+  if (M < 1 || M > (1 << 20)) return MOE_ERR_SHAPE;
+  if (N < 128 || N % 128 || K < 128 || K % 128) return MOE_ERR_SHAPE;
+  if (N > (1 << 16) || K > (1 << 16) || (long long)N * K >= (1LL << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+void make_linear_layout(int M, int N, int K, LinearLayout& L) {
+  (void)N;
+  L.BM = pick_block_m(M, 1, 1);
+  L.nblk = (M + L.BM - 1) / L.BM;
+  L.cap = (size_t)L.nblk * L.BM;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = round_up(o + bytes, kAlign);
+    return at;
+  };
+  L.xq = take(L.cap * K);            // rows past M: never written, read as padding
+  L.xs = take(L.cap * (K / 128) * 4);
+  L.sorted = take(L.cap * 4);
+  L.eids = take((size_t)L.nblk * 4);
+  L.meta = take(16);                 // eoff[2], ntpp
+  L.dump = take(512);
+  L.total = o;
 }
 
 }  // namespace
@@ -253,6 +287,46 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m, int
                            nullptr, scratch, stream)
              ? MOE_ERR_HIP
              : MOE_OK;
+}
+
+size_t fp8_block_linear_workspace_bytes(int M, int N, int K) {
+  if (check_linear_shape(M, N, K) != MOE_OK) return 0;
+  LinearLayout L;
+  make_linear_layout(M, N, K, L);
+  return L.total;
+}
+
+int fp8_block_linear(const void* x, const uint8_t* w, const float* w_scale, int M, int N, int K,
+                     void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_linear_shape(M, N, K);
+  if (st != MOE_OK) return st;
+  if (!x || !w || !w_scale || !out || !workspace) return MOE_ERR_NULL;
+  if ((uintptr_t)x % 16 || (uintptr_t)w % 16 || (uintptr_t)w_scale % 4 || (uintptr_t)out % 16 ||
+      (uintptr_t)workspace % kAlign)
+    return MOE_ERR_UNSUPPORTED;
+  LinearLayout L;
+  make_linear_layout(M, N, K, L);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const size_t xb = (size_t)M * K * 2, ob = (size_t)M * N * 2;
+  const size_t wb = (size_t)N * K, sb = (size_t)(N / 128) * (K / 128) * 4;
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || overlaps(out, ob, w_scale, sb) ||
+      overlaps(workspace, L.total, x, xb) || overlaps(workspace, L.total, w, wb) ||
+      overlaps(workspace, L.total, w_scale, sb) || overlaps(workspace, L.total, out, ob))
+    return MOE_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  uint8_t* xq = (uint8_t*)(ws + L.xq);
+  float* xs = (float*)(ws + L.xs);
+  int32_t* sorted = (int32_t*)(ws + L.sorted);
+  int32_t* eids = (int32_t*)(ws + L.eids);
+  int32_t* eoff = (int32_t*)(ws + L.meta);
+  int32_t* ntpp = eoff + 2;
+  uint16_t* dump = (uint16_t*)(ws + L.dump);
+  if (moe::launch_group_quant(x, M, K, xq, xs, stream)) return MOE_ERR_HIP;
+  if (moe::launch_identity_layout(M, L.BM, L.nblk, sorted, eids, eoff, ntpp, stream)) return MOE_ERR_HIP;
+  if (moe::launch_gemm2_bounded(xq, xs, w, w_scale, sorted, eids, ntpp, eoff, N, K, M, L.BM, L.nblk,
+                                (uint16_t*)out, N, M, N, dump, stream))
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -203,6 +203,33 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
               void* scratch, size_t scratch_bytes, hipStream_t stream);
 
 /* Static description of a moe_status code. */
+/*
+ * Dense block-FP8 linear layer (overview page, "W8A8BlockFp8LinearOp - Block
+ * FP8 GEMM Dispatch": the block-wise FP8 GEMM of DeepSeek-V3-style dense
+ * layers, with the weights on the MFMA's M side for small token counts as the
+ * section's swapAB path does; scales as in "Weight Scale Granularities": a
+ * dynamic 128-group scale per token row, a static scale per 128x128 weight
+ * block):
+ *   (xq, xs) = per_token_group_quant_fp8(x)
+ *   out[m, n] = bf16_RNE( sum_kb xs[m, kb] * w_scale[n/128, kb]
+ *                          * sum_{k in kb} dec(xq[m, k]) * dec(w[n, k]) )
+ * accumulated in float32 on FP8 MFMAs (the E = 1 case of the second grouped
+ * GEMM).
+ *
+ *   x        bf16    [M, K]          device, 16-byte aligned
+ *   w        e4m3fn  [N, K]          device, row-major (one output per row)
+ *   w_scale  float32 [N/128, K/128]  device, dequantisation multipliers
+ *   out      bf16    [M, N]          device, must not overlap any input
+ *   workspace: fp8_block_linear_workspace_bytes(M, N, K) bytes, 256-byte
+ *   aligned, caller-owned, contents undefined on return.
+ * Constraints: 1 <= M <= 2^20; N and K positive multiples of 128, each
+ * <= 65536, N*K < 2^31.  Returns MOE_OK or a negative moe_status (checked
+ * before anything is enqueued); out is undefined on error.
+ */
+size_t fp8_block_linear_workspace_bytes(int M, int N, int K);
+int fp8_block_linear(const void* x, const uint8_t* w, const float* w_scale, int M, int N, int K,
+                     void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 const char* moe_status_string(int status);
 
 #ifdef __cplusplus
