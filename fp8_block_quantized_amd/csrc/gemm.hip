@@ -64,7 +64,9 @@ struct GemmArgs {
   int split;                 // workgroups per row block (BM / rows per workgroup)
   int y_stride;              // GEMM2: row stride of y_out (H rounded up to 256)
   int y_rows, y_cols;        // GEMM2: stored region of y_out; other stores go to y_dump
-  uint16_t* y_dump;          // GEMM2: 512 bytes
+  uint16_t* y_dump;          // GEMM2: 1024 bytes
+  int ksplit;                // GEMM2 prefill: K slices per tile (1: bf16 y_out)
+  float* part;               // GEMM2, ksplit > 1: float32 partials [ksplit, y_rows, y_stride]
 };
 
 // M0 is written only inside these statements, each right before its load;
@@ -528,19 +530,23 @@ constexpr int kRingW = 256 * 128;      // 256 weight rows x one 128-byte K block
 // earlier may still be in flight (vector memory operations retire in order).
 // The epilogue therefore stores unconditionally (the output has whole
 // 256-feature tiles per row, padding rows included) and issues no loads.
-// Needs at least two K blocks per tile.
+// Needs at least two K blocks per tile.  A tile may cover one of ksplit equal
+// K slices (for outputs with few tiles): it then stores float32 partials,
+// which a reduction kernel sums in slice order.
 constexpr int kPf2Loads = 7;               // DMA instructions per wave per stage
 constexpr int kPf2Stores = 16;             // output stores per wave per tile
 constexpr int kPf2S = 2048;                // token scales, eight 256-byte wave slots
 
 struct TileId {
-  int e, b, j;
+  int e, b, j, ks;
 };
 
 // Logical tile L -> (expert, m block, n tile) in expert-major order, by a
 // binary search over the expert block offsets.  Scalar loads only: they stay
 // out of the vector memory counter that the ring's waits rely on.
-__device__ __forceinline__ TileId tile_id(int L, const GemmArgs& a) {
+__device__ __forceinline__ TileId tile_id(int L, const GemmArgs& a, int ksplit) {
+  const int ks = L % ksplit;
+  L /= ksplit;
   const int nt = a.n_tiles;
   int lo = 0, hi = a.E - 1;
   while (lo < hi) {
@@ -549,9 +555,10 @@ __device__ __forceinline__ TileId tile_id(int L, const GemmArgs& a) {
   }
   const int b0 = load_uniform(a.eoff + lo), nb = load_uniform(a.eoff + lo + 1) - b0;
   const int local = L - b0 * nt, j = local / nb;
-  return {lo, b0 + (local - j * nb), j};
+  return {lo, b0 + (local - j * nb), j, ks};
 }
 
+template <bool kSplitK>
 __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   constexpr int BM = 128;
   constexpr int kA = BM * 128, kStage = kRingW + kA + kPf2S;
@@ -561,16 +568,18 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   const int wt = wave >> 2, wf = wave & 3;
   const int g = lane >> 4, l16 = lane & 15;
   const int K = args.K, nkb = K >> 7, N = args.N;
+  const int ksplit = kSplitK ? args.ksplit : 1;
+  const int nkb_t = nkb / ksplit;         // K blocks of one tile's slice
 
   // this workgroup's tiles
-  const int n_real = load_uniform(args.eoff + args.E) * args.n_tiles;
+  const int n_real = load_uniform(args.eoff + args.E) * args.n_tiles * ksplit;
   const int per_xcd = gridDim.x >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int q8 = n_real >> 3, r8 = n_real & 7;
   const int xbeg = xcd * q8 + (xcd < r8 ? xcd : r8), xcnt = q8 + (xcd < r8 ? 1 : 0);
   const int ntile = slot < xcnt ? (xcnt - 1 - slot) / per_xcd + 1 : 0;
   if (ntile == 0) return;
-  const int G = ntile * nkb;
-  auto tile_at = [&](int i) { return tile_id(xbeg + slot + i * per_xcd, args); };
+  const int G = ntile * nkb_t;
+  auto tile_at = [&](int i) { return tile_id(xbeg + slot + i * per_xcd, args, ksplit); };
 
   // this lane's 16-byte pieces of a stage: weight rows (wave*4 + i)*8 + lr of
   // the tile's 256, token rows (wave*2 + i)*8 + lr of its 128, chunk lc under
@@ -589,9 +598,10 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   const uint32_t soff = (uint32_t)(((wave & 1) * 64 + lane) * nkb * 4);
   auto issue = [&](int stage, const TileId& t, const uint32_t (&wo)[4], int kb) {
     const uint32_t base = lds_offset(ring + stage * kStage);
-    const uint8_t* wb = args.w + (size_t)t.e * N * K + (size_t)kb * 128;
-    const uint8_t* ab = args.act + (size_t)t.b * BM * K + (size_t)kb * 128;
-    const uint8_t* sb = (const uint8_t*)(args.act_scale + (size_t)t.b * BM * nkb + kb);
+    const int kg = t.ks * nkb_t + kb;      // K block within the full reduction
+    const uint8_t* wb = args.w + (size_t)t.e * N * K + (size_t)kg * 128;
+    const uint8_t* ab = args.act + (size_t)t.b * BM * K + (size_t)kg * 128;
+    const uint8_t* sb = (const uint8_t*)(args.act_scale + (size_t)t.b * BM * nkb + kg);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16s(wo[i], wb, base + (wave * 4 + i) * 1024);
 #pragma unroll
@@ -626,7 +636,7 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
     for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[pp][q] = zero;
-    for (int kb = 0; kb < nkb; ++kb, ++s) {
+    for (int kb = 0; kb < nkb_t; ++kb, ++s) {
       const bool more = s + 1 < G, stores = ti > 0 && kb < 2;
       if (more) {
         if (stores) wait_vmem<kPf2Loads + kPf2Stores>(); else wait_vmem<kPf2Loads>();
@@ -635,11 +645,11 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
       }
       barrier_raw();
       if (s + 2 < G) {
-        if (kb + 2 < nkb) issue((s + 2) % kRingStages, cur, cwo, kb + 2);
-        else issue((s + 2) % kRingStages, nxt, nwo, kb + 2 - nkb);
+        if (kb + 2 < nkb_t) issue((s + 2) % kRingStages, cur, cwo, kb + 2);
+        else issue((s + 2) % kRingStages, nxt, nwo, kb + 2 - nkb_t);
       }
       const uint8_t* st = ring + (s % kRingStages) * kStage;
-      const float sw = load_uniform(wsp + kb);
+      const float sw = load_uniform(wsp + cur.ks * nkb_t + kb);
       v8i pf[4];
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
@@ -669,13 +679,18 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
         const int col = nf + 16 * pp + 4 * g;
-        uint16_t* dst = row < args.y_rows && col < args.y_cols
-                            ? args.y_out + (size_t)row * args.y_stride + col
-                            : args.y_dump + 4 * lane;
-        uint2 v;
-        v.x = f32_to_bf16_bits(acc[pp][q][0]) | (f32_to_bf16_bits(acc[pp][q][1]) << 16);
-        v.y = f32_to_bf16_bits(acc[pp][q][2]) | (f32_to_bf16_bits(acc[pp][q][3]) << 16);
-        *(uint2*)dst = v;
+        const bool in = row < args.y_rows && col < args.y_cols;
+        if (!kSplitK) {
+          uint16_t* dst = in ? args.y_out + (size_t)row * args.y_stride + col : args.y_dump + 4 * lane;
+          uint2 v;
+          v.x = f32_to_bf16_bits(acc[pp][q][0]) | (f32_to_bf16_bits(acc[pp][q][1]) << 16);
+          v.y = f32_to_bf16_bits(acc[pp][q][2]) | (f32_to_bf16_bits(acc[pp][q][3]) << 16);
+          *(uint2*)dst = v;
+        } else {     // float32 partial of K slice ks
+          float* dst = in ? args.part + ((size_t)cur.ks * args.y_rows + row) * args.y_stride + col
+                          : (float*)args.y_dump + 4 * lane;
+          *(float4*)dst = make_float4(acc[pp][q][0], acc[pp][q][1], acc[pp][q][2], acc[pp][q][3]);
+        }
       }
     }
     if (ti + 1 < ntile) {
@@ -866,19 +881,52 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
   }
 }
 
+// Sum of the float32 K-slice partials in slice order, rounded once to bf16:
+// out[r, c] = bf16( sum_s part[s, r, c] ) for r < rows, c < cols (cols % 8 == 0).
+__global__ __launch_bounds__(256) void reduce_slices_kernel(const float4* __restrict__ part,
+                                                            int ksplit, int rows, int cols8,
+                                                            uint4* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;   // 8 outputs per thread
+  const long long n = (long long)rows * cols8;
+  if (i >= n) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < ksplit; ++s) {
+    const float4 a = part[2 * (s * n + i)], b = part[2 * (s * n + i) + 1];
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+  uint4 o;
+  o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+  o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+  o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
+  o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+  out[i] = o;
+}
+
+static hipError_t launch_reduce_slices(const float* part, int ksplit, int rows, int cols,
+                                       uint16_t* out, hipStream_t stream) {
+  const long long n = (long long)rows * (cols / 8);
+  hipLaunchKernelGGL(reduce_slices_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     (const float4*)part, ksplit, rows, cols / 8, (uint4*)out);
+  return hipGetLastError();
+}
+
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
-  if (BM == 128 && a.K >= 256) {
+  if (BM == 128 && (a.K >> 7) / a.ksplit >= 2) {
     // one persistent workgroup per CU, a multiple of the 8 XCDs
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidDevice;
-    const long long tiles = (long long)a.nblk * a.n_tiles;
+    const long long tiles = (long long)a.nblk * a.n_tiles * a.ksplit;
     long long wg = cus / 8 * 8;
     if (wg > (tiles + 7) / 8 * 8) wg = (tiles + 7) / 8 * 8;
     if (wg < 8) wg = 8;
-    hipLaunchKernelGGL(moe_gemm2_pf_kernel, dim3((unsigned)wg), dim3(512), 0, stream, a);
+    if (a.ksplit > 1)
+      hipLaunchKernelGGL(moe_gemm2_pf_kernel<true>, dim3((unsigned)wg), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL(moe_gemm2_pf_kernel<false>, dim3((unsigned)wg), dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   switch (BM) {
@@ -930,7 +978,7 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
   a.act = aq; a.act_scale = as; a.w = w2; a.w_scale = w2s;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
   a.y_out = y; a.y_stride = y_stride;
-  a.y_rows = nblk * BM; a.y_cols = y_stride; a.y_dump = y;
+  a.y_rows = nblk * BM; a.y_cols = y_stride; a.y_dump = y; a.ksplit = 1;
   a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
   a.n_tiles = (H + 255) / 256; a.nblk = nblk;
   return launch_gemm2_bm(a, BM, stream);
@@ -940,16 +988,20 @@ hipError_t launch_gemm2_bounded(const uint8_t* act, const float* act_scale, cons
                                 const float* w_scale, const int32_t* sorted_ids,
                                 const int32_t* expert_ids, const int32_t* ntpp, const int32_t* eoff,
                                 int N, int K, int P, int BM, int nblk, uint16_t* y, int y_stride,
-                                int y_rows, int y_cols, uint16_t* y_dump, hipStream_t stream) {
+                                int y_rows, int y_cols, uint16_t* y_dump, int ksplit, float* part,
+                                hipStream_t stream) {
   GemmArgs a{};
   a.eoff = eoff; a.E = 1; a.split = 1;
   a.act = act; a.act_scale = act_scale; a.w = w; a.w_scale = w_scale;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
   a.y_out = y; a.y_stride = y_stride;
   a.y_rows = y_rows; a.y_cols = y_cols; a.y_dump = y_dump;
+  a.ksplit = ksplit; a.part = part;
   a.K = K; a.N = N; a.I = K; a.H = N; a.P = P; a.top_k = 1;
   a.n_tiles = (N + 255) / 256; a.nblk = nblk;
-  return launch_gemm2_bm(a, BM, stream);
+  hipError_t err = launch_gemm2_bm(a, BM, stream);
+  if (err != hipSuccess || ksplit == 1) return err;
+  return launch_reduce_slices(part, ksplit, y_rows, y_cols, y, stream);
 }
 
 }  // namespace moe

@@ -74,11 +74,32 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
-// Dense linear: one expert owning every row, in blocks of BM rows.
+// Dense linear: one expert owning every row, in blocks of 128 rows (the
+// persistent GEMM), the reduction split into ksplit equal K slices when the
+// output has too few tiles to give each of the 256 workgroups work.
 struct LinearLayout {
-  int BM, nblk;
-  size_t cap, xq, xs, sorted, eids, meta, dump, total;
+  int BM, nblk, ksplit;
+  size_t cap, xq, xs, sorted, eids, meta, dump, part, total;
 };
+
+// The divisor of the K-block count that minimises the K blocks the busiest
+// of 256 workgroups streams (at least two per slice); ties to fewer slices.
+int pick_ksplit(int nblk, int N, int K) {
+  constexpr long long kWorkgroups = 256;
+  const long long tiles = (long long)nblk * ((N + 255) / 256);
+  const int nkb = K / 128;
+  int best = 1;
+  long long best_cost = (tiles + kWorkgroups - 1) / kWorkgroups * nkb;
+  for (int d = 2; d <= nkb / 2; ++d) {
+    if (nkb % d) continue;
+    const long long cost = (tiles * d + kWorkgroups - 1) / kWorkgroups * (nkb / d);
+    if (cost < best_cost) {
+      best = d;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 int check_linear_shape(int M, int N, int K) {
   if (M < 1 || M > (1 << 20)) return MOE_ERR_SHAPE;
@@ -88,9 +109,9 @@ int check_linear_shape(int M, int N, int K) {
 }
 
 void make_linear_layout(int M, int N, int K, LinearLayout& L) {
-  (void)N;
-  L.BM = pick_block_m(M, 1, 1);
+  L.BM = 128;
   L.nblk = (M + L.BM - 1) / L.BM;
+  L.ksplit = pick_ksplit(L.nblk, N, K);
   L.cap = (size_t)L.nblk * L.BM;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -103,7 +124,8 @@ void make_linear_layout(int M, int N, int K, LinearLayout& L) {
   L.sorted = take(L.cap * 4);
   L.eids = take((size_t)L.nblk * 4);
   L.meta = take(16);                 // eoff[2], ntpp
-  L.dump = take(512);
+  L.dump = take(1024);
+  L.part = take(L.ksplit > 1 ? (size_t)L.ksplit * M * N * 4 : 0);
   L.total = o;
 }
 
@@ -321,10 +343,11 @@ int fp8_block_linear(const void* x, const uint8_t* w, const float* w_scale, int 
   int32_t* eoff = (int32_t*)(ws + L.meta);
   int32_t* ntpp = eoff + 2;
   uint16_t* dump = (uint16_t*)(ws + L.dump);
+  float* part = (float*)(ws + L.part);
   if (moe::launch_group_quant(x, M, K, xq, xs, stream)) return MOE_ERR_HIP;
   if (moe::launch_identity_layout(M, L.BM, L.nblk, sorted, eids, eoff, ntpp, stream)) return MOE_ERR_HIP;
   if (moe::launch_gemm2_bounded(xq, xs, w, w_scale, sorted, eids, ntpp, eoff, N, K, M, L.BM, L.nblk,
-                                (uint16_t*)out, N, M, N, dump, stream))
+                                (uint16_t*)out, N, M, N, dump, L.ksplit, part, stream))
     return MOE_ERR_HIP;
   return MOE_OK;
 }

@@ -137,3 +137,32 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(TypeError):
         moe.per_token_group_quant_fp8(torch.zeros((2, 128), dtype=torch.bfloat16),
                                       q=torch.zeros(1), scales=torch.zeros(1))
+
+
+def test_linear_workspace_and_argument_checks():
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    M, N, K = 64, 256, 512
+    need = moe.fp8_block_linear_workspace_bytes(M, N, K)
+    assert need > 0
+    assert moe.fp8_block_linear_workspace_bytes(M, N + 64, K) == 0      # N % 128
+    assert moe.fp8_block_linear_workspace_bytes(0, N, K) == 0
+    assert moe.fp8_block_linear_workspace_bytes(M, 65536, 65536) == 0  # N*K >= 2^31
+    assert moe.fp8_block_linear_workspace_bytes(2 * M, N, K) >= need
+    x, w, s, out = (vp(0x10000 * i) for i in (1, 2, 3, 4))
+    ws = vp(0x7000000000)
+
+    def call(*a):
+        return lib.fp8_block_linear(*a)
+
+    ok = [x, w, s, M, N, K, out, ws, need, None]
+    bad = list(ok); bad[5] = 100
+    assert call(*bad) == -2                      # shape
+    bad = list(ok); bad[0] = None
+    assert call(*bad) == -1                      # null
+    bad = list(ok); bad[8] = need - 1
+    assert call(*bad) == -4                      # workspace too small
+    bad = list(ok); bad[6] = vp(0x10000 + 16)
+    assert call(*bad) == -6                      # out overlaps x
+    bad = list(ok); bad[7] = vp(0x7000000000 + 8)
+    assert call(*bad) == -3                      # workspace misaligned
