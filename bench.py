@@ -10,7 +10,8 @@ T=64 tokens plus one prefill batch of T=8192 tokens through the whole path
 (router, sort-and-pad, activation quant, GEMM1 + SiLU*mul + requant, GEMM2 +
 routing weight, combine).  Inputs are resident in HBM before timing starts.
 The standalone activation quantiser is also timed on its own workload, bf16
-[16384, 7168] with 1% x100 outliers.
+[16384, 7168] with 1% x100 outliers, and the dense block-FP8 linear on a
+DeepSeek-V3-shaped down projection (7168 x 18432) at M = 64 and 8192.
 
 Prints one JSON line.  value = tokens per second over the step.
 """
@@ -243,6 +244,30 @@ def main():
     quant = {"M": M, "K": K, "ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
              "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
 
+    # dense block-FP8 linear (the layer's E = 1 neighbour), decode and prefill batches
+    from synth import LINEAR_WORKLOAD, make_linear
+    LN, LK = LINEAR_WORKLOAD["N"], LINEAR_WORKLOAD["K"]
+    dense = {"workload": f"DeepSeek-V3-shaped dense down projection N={LN} K={LK}"}
+    for LM in LINEAR_WORKLOAD["M"]:
+        lx, lw, lws = make_linear(LM, LN, LK, 1000 * LINEAR_WORKLOAD["index"], device=dev)
+        lout = torch.empty((LM, LN), dtype=torch.bfloat16, device=dev)
+        lwsp = torch.empty(moe.fp8_block_linear_workspace_bytes(LM, LN, LK), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            moe.fp8_block_linear(lx, lw, lws, out=lout, workspace=lwsp)
+        le = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        le[0].record()
+        for _ in range(args.steps):
+            moe.fp8_block_linear(lx, lw, lws, out=lout, workspace=lwsp)
+        le[1].record()
+        torch.cuda.synchronize()
+        lms = le[0].elapsed_time(le[1]) / args.steps
+        lbytes = LN * LK + 4 * (LN // 128) * (LK // 128) + 2 * LM * LK + 2 * LM * LN
+        r = roofline_of(lbytes, 2 * LM * LN * LK, lms * 1e-3, MFMA_FP8_PEAK)
+        r.update({"M": LM, "ms": lms, "alg_bytes": lbytes, "alg_flops": 2 * LM * LN * LK})
+        dense[f"M{LM}"] = r
+        del lx, lw, lws, lout, lwsp
+
     dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
     dom = kernels[dom_name]
     roof = roofline_of(dom["bytes"], dom["flops"], dom["ms"] * 1e-3, dom["peak"])
@@ -271,6 +296,7 @@ def main():
         "roofline": roof,
         "phases": result_phases,
         "quant_standalone": quant,
+        "dense_linear": dense,
     }
     if not args.no_cpu_baseline and "decode" in phases:
         ph = phases["decode"]
