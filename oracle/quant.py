@@ -26,7 +26,8 @@ decision.
 
 Pinned by tests/test_oracle_quant.py (scalar brute-force loop, invariants
 on the maximum code, the exact scale, the dequant error bound and the
-all-zero and negative-zero cases).
+all-zero and negative-zero cases).  per_token_group_quant_pow2 (power-of-two
+scales, groups of 32 or 128) is pinned in tests/test_oracle_quant_pow2.py.
 """
 
 import numpy as np
@@ -72,3 +73,40 @@ def block_dequant(w, ws, block: int = 128) -> np.ndarray:
     scale = np.repeat(np.repeat(np.asarray(ws, dtype=np.float64), block, axis=0),
                       block, axis=1)
     return d * scale
+
+
+def ceil_pow2(s) -> np.ndarray:
+    """float32 s > 0 -> the smallest power of two >= s, as float32: the scale
+    rounded up to an unsigned 8-bit exponent with no mantissa (UE8M0)."""
+    s = np.asarray(s, dtype=np.float32)
+    m, e = np.frexp(s.astype(np.float64))          # s = m * 2^e, 0.5 <= m < 1
+    return np.where(m == 0.5, s.astype(np.float64), np.ldexp(1.0, e)).astype(np.float32)
+
+
+def per_token_group_quant_pow2(x, group: int = GROUP):
+    """Power-of-two group scales.
+
+    Sources: overview page, "DeepGEMM Scale Formats" (FLOAT32_CEIL_UE8M0:
+    float32 scales rounded up to UE8M0; UE8M0: the same exponents packed as
+    bytes, four per int32); fp8 oracle API page, the MXFP8 [1, 32] block
+    shape whose activation scales are uint8 UE8M0 values laid out
+    (num_tokens, hidden // 32).  Definition, per row and group of `group`
+    (32 or 128) consecutive columns:
+      s = ceil_pow2(float32(max(amax, 1e-8)) / 448)    (the float32 scale of
+                                                         per_token_group_quant,
+                                                         rounded up)
+      q = e4m3.encode(float32(x / s))                   (exact: s is a power of two)
+      e = log2(s) + 127                                 (the UE8M0 byte)
+    Rounding up keeps |x / s| <= 448, so no value saturates.
+    Returns (q uint8 [M, K], s float32 [M, K // group], e uint8 [M, K // group])."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    xg = x.reshape(M, K // group, group)
+    amax = np.max(np.abs(xg), axis=2)
+    s = ceil_pow2((np.maximum(amax, AMAX_EPS).astype(np.float32) / FP8_MAX).astype(np.float32))
+    quot = (xg / s[:, :, None]).astype(np.float32)
+    q = e4m3.encode(quot).reshape(M, K)
+    ex = (np.frexp(s.astype(np.float64))[1] - 1 + 127).astype(np.uint8)
+    return q, s, ex
