@@ -27,7 +27,8 @@ QUANT_GROUP = 128
 STAGES = ["router", "align", "quant", "gemm1", "gemm2", "combine"]
 
 EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layout",
-           "moe_fp8_forward", "moe_fp8_forward_traced", "per_token_group_quant_fp8", "moe_topk_softmax",
+           "moe_fp8_forward", "moe_fp8_forward_traced", "per_token_group_quant_fp8",
+           "per_token_group_quant_fp8_fmt", "moe_topk_softmax",
            "moe_align_scratch_bytes", "moe_align", "moe_status_string",
            "fp8_block_linear_workspace_bytes", "fp8_block_linear"]
 
@@ -63,6 +64,8 @@ def load_library(path=LIB_PATH):
     lib.moe_fp8_forward_traced.restype = c_int
     lib.per_token_group_quant_fp8.argtypes = [vp, c_int, c_int, c_int, vp, vp, vp]
     lib.per_token_group_quant_fp8.restype = c_int
+    lib.per_token_group_quant_fp8_fmt.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp]
+    lib.per_token_group_quant_fp8_fmt.restype = c_int
     lib.moe_topk_softmax.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp]
     lib.moe_topk_softmax.restype = c_int
     lib.moe_align_scratch_bytes.argtypes = [c_int] * 3
@@ -196,6 +199,27 @@ def per_token_group_quant_fp8(x, group_size=128, q=None, scales=None, stream=Non
         _dev(x, torch.bfloat16, "x"), M, K, group_size, _dev(q, torch.uint8, "q"),
         _dev(scales, torch.float32, "scales"), _stream(stream))
     _check("per_token_group_quant_fp8", st)
+    return q, scales
+
+
+SCALE_FORMATS = {"float32": 0, "float32_ceil_ue8m0": 1, "ue8m0": 2}
+
+
+def per_token_group_quant_fp8_fmt(x, group_size=128, scale_format="float32", q=None, scales=None,
+                                  stream=None):
+    """x bf16 [M, K] -> (q uint8 e4m3fn codes [M, K], scales [M, K/group]): float32
+    scales for "float32" and "float32_ceil_ue8m0", uint8 exponent bytes for "ue8m0"."""
+    M, K = x.shape
+    fmt = SCALE_FORMATS[scale_format]
+    sdt = torch.uint8 if scale_format == "ue8m0" else torch.float32
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // group_size), dtype=sdt, device=x.device)
+    st = load_library().per_token_group_quant_fp8_fmt(
+        _dev(x, torch.bfloat16, "x"), M, K, group_size, fmt, _dev(q, torch.uint8, "q"),
+        _dev(scales, sdt, "scales"), _stream(stream))
+    _check("per_token_group_quant_fp8_fmt", st)
     return q, scales
 
 

@@ -7,8 +7,13 @@
 
 namespace moe {
 
+// Scale formats of the group quantiser (values of the public format enum).
+enum { kScaleFloat32 = 0, kScaleFloat32CeilUe8m0 = 1, kScaleUe8m0 = 2 };
 hipError_t launch_group_quant(const void* x, long long M, int K, uint8_t* q, float* s,
                               hipStream_t stream);
+// group 32 or 128, fmt one of the kScale* values; s is float32 or uint8 per group
+hipError_t launch_group_quant_fmt(const void* x, long long M, int K, int group, int fmt,
+                                  uint8_t* q, void* s, hipStream_t stream);
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int top_k, int renormalize,
                                int32_t* ids, float* w, hipStream_t stream);
 size_t align_scratch_bytes(int P, int E);

@@ -275,6 +275,25 @@ int per_token_group_quant_fp8(const void* x, int M, int K, int group_size, uint8
   return moe::launch_group_quant(x, M, K, q, scales, stream) ? MOE_ERR_HIP : MOE_OK;
 }
 
+int per_token_group_quant_fp8_fmt(const void* x, int M, int K, int group_size, int scale_format,
+                                  uint8_t* q, void* scales, hipStream_t stream) {
+  if (group_size != 32 && group_size != 128) return MOE_ERR_UNSUPPORTED;
+  if (scale_format < MOE_SCALE_FLOAT32 || scale_format > MOE_SCALE_UE8M0)
+    return MOE_ERR_UNSUPPORTED;
+  if (M < 0 || K < group_size || K % group_size) return MOE_ERR_SHAPE;
+  if ((long long)M * K > (1LL << 40)) return MOE_ERR_SHAPE;
+  if (M == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_NULL;
+  const size_t sb = scale_format == MOE_SCALE_UE8M0 ? 1 : 4;
+  if ((uintptr_t)x % 16 || (uintptr_t)q % 8 || (uintptr_t)scales % sb) return MOE_ERR_UNSUPPORTED;
+  const size_t n = (size_t)M * K, ns = n / group_size * sb;
+  if (overlaps(q, n, x, 2 * n) || overlaps(scales, ns, x, 2 * n) || overlaps(q, n, scales, ns))
+    return MOE_ERR_ALIAS;
+  return moe::launch_group_quant_fmt(x, M, K, group_size, scale_format, q, scales, stream)
+             ? MOE_ERR_HIP
+             : MOE_OK;
+}
+
 int moe_topk_softmax(const float* logits, int T, int E, int top_k, int renormalize,
                      int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
   if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || top_k < 1 || top_k > E || top_k > MOE_MAX_TOP_K)

@@ -1,28 +1,41 @@
-// Per-token, per-128-group dynamic FP8 (e4m3fn) activation quantisation.
+// Per-token, per-group dynamic FP8 (e4m3fn) activation quantisation.
 //
 // Operation (fp8 oracle API page, activation quant key kFp8Dynamic128Sym;
 // overview page, "Weight Scale Granularities", GROUP = one scale per 128
 // consecutive elements): for each row and group of 128 columns,
 //   s = max(amax, 1e-8) / 448,  q = e4m3fn_RNE_saturate(x / s).
+// Power-of-two variants (overview page, "DeepGEMM Scale Formats": float32
+// scales rounded up to UE8M0, or the UE8M0 exponent bytes themselves; fp8
+// oracle API page, the MXFP8 [1, 32] activation quant with uint8 UE8M0
+// scales): the same float32 s rounded up to the next power of two, for
+// groups of 32 or 128.  A power-of-two scale makes x / s an exact scaling,
+// and rounding up keeps |x / s| <= 448.
 //
-// The row-major [M, K] input with K a multiple of 128 is a flat sequence of
-// M*K/128 groups of 128 bf16 (256 bytes).  Sixteen lanes own one group, each
-// lane 8 consecutive values (one 16-byte load), so a wave covers four groups
-// (1 KiB of contiguous input) per step and every access is a full, aligned
-// vector load or store.  The group amax is a 16-lane butterfly; the scale and
-// its reciprocal are computed once per lane, and every element costs one
-// multiply and two FMAs for the correctly rounded quotient.  HBM bound: 2
-// bytes in, 1 byte + 4/128 bytes out per element.
+// The row-major [M, K] input with K a multiple of the group is a flat
+// sequence of M*K/G groups of G bf16 values.  G/8 lanes own one group, each
+// lane 8 consecutive values (one 16-byte load), so a wave covers 1 KiB of
+// contiguous input per step and every access is a full, aligned vector load
+// or store.  The group amax is a butterfly over its lanes; the scale and its
+// reciprocal are computed once per lane, and every element costs one
+// multiply and two FMAs for the correctly rounded quotient (one multiply for
+// a power-of-two scale).  HBM bound: 2 bytes in, 1 byte + 4/G (or 1/G)
+// bytes out per element.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
-template <int SLOTS>
+// float32 s > 0 (normal) -> the smallest power of two >= s, as its bits.
+__device__ __forceinline__ uint32_t ceil_pow2_bits(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return (b & 0x7FFFFFu) ? (b & 0x7F800000u) + 0x00800000u : b;
+}
+
+template <int G, int FMT, int SLOTS>
 __global__ __launch_bounds__(256) void group_quant_bf16_kernel(
-    const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scales,
+    const uint4* __restrict__ x, uint2* __restrict__ q, void* __restrict__ scales,
     long long nslots) {
-  // slot = one lane's 8 elements; 16 slots per group
+  constexpr int LPG = G / 8;   // lanes per group
   const long long base = ((long long)blockIdx.x * 256 * SLOTS) + threadIdx.x;
   uint4 v[SLOTS];
 #pragma unroll
@@ -41,31 +54,65 @@ __global__ __launch_bounds__(256) void group_quant_bf16_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
-    amax = wave_max_xor(amax, 8, 1);   // the 16 lanes of this group
+    amax = wave_max_xor(amax, LPG / 2, 1);   // the lanes of this group
     float s, r;
     group_scale(amax, s, r);
+    float d[8];
+    if (FMT == kScaleFloat32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d[i] = clamp_fp8(div_by_scale(f[i], s, r));
+    } else {
+      const uint32_t sb = ceil_pow2_bits(s);
+      s = __uint_as_float(sb);
+      r = __uint_as_float((254u - (sb >> 23)) << 23);   // exactly 1 / s
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d[i] = clamp_fp8(f[i] * r);
+    }
     uint2 out;
-    out.x = pack4_e4m3(clamp_fp8(div_by_scale(f[0], s, r)), clamp_fp8(div_by_scale(f[1], s, r)),
-                       clamp_fp8(div_by_scale(f[2], s, r)), clamp_fp8(div_by_scale(f[3], s, r)));
-    out.y = pack4_e4m3(clamp_fp8(div_by_scale(f[4], s, r)), clamp_fp8(div_by_scale(f[5], s, r)),
-                       clamp_fp8(div_by_scale(f[6], s, r)), clamp_fp8(div_by_scale(f[7], s, r)));
+    out.x = pack4_e4m3(d[0], d[1], d[2], d[3]);
+    out.y = pack4_e4m3(d[4], d[5], d[6], d[7]);
     if (slot < nslots) {
       q[slot] = out;
-      if ((threadIdx.x & 15) == 0) scales[slot >> 4] = s;
+      if ((threadIdx.x & (LPG - 1)) == 0) {
+        if (FMT == kScaleUe8m0)
+          ((uint8_t*)scales)[slot / LPG] = (uint8_t)(__float_as_uint(s) >> 23);
+        else
+          ((float*)scales)[slot / LPG] = s;
+      }
     }
   }
 }
 
-hipError_t launch_group_quant(const void* x, long long M, int K, uint8_t* q, float* s,
-                              hipStream_t stream) {
-  const long long nslots = M * (long long)(K / 8);
-  if (nslots == 0) return hipSuccess;
+template <int G, int FMT>
+static hipError_t launch_quant_t(const void* x, long long nslots, uint8_t* q, void* s,
+                                 hipStream_t stream) {
   constexpr int SLOTS = 2;
   const long long per_block = 256LL * SLOTS;
   const long long nblk = (nslots + per_block - 1) / per_block;
-  hipLaunchKernelGGL(group_quant_bf16_kernel<SLOTS>, dim3((unsigned)nblk), dim3(256), 0, stream,
-                     (const uint4*)x, (uint2*)q, s, nslots);
+  hipLaunchKernelGGL((group_quant_bf16_kernel<G, FMT, SLOTS>), dim3((unsigned)nblk), dim3(256), 0,
+                     stream, (const uint4*)x, (uint2*)q, s, nslots);
   return hipGetLastError();
+}
+
+hipError_t launch_group_quant_fmt(const void* x, long long M, int K, int group, int fmt,
+                                  uint8_t* q, void* s, hipStream_t stream) {
+  const long long nslots = M * (long long)(K / 8);
+  if (nslots == 0) return hipSuccess;
+  if (group == 128) {
+    if (fmt == kScaleFloat32) return launch_quant_t<128, kScaleFloat32>(x, nslots, q, s, stream);
+    if (fmt == kScaleFloat32CeilUe8m0)
+      return launch_quant_t<128, kScaleFloat32CeilUe8m0>(x, nslots, q, s, stream);
+    return launch_quant_t<128, kScaleUe8m0>(x, nslots, q, s, stream);
+  }
+  if (fmt == kScaleFloat32) return launch_quant_t<32, kScaleFloat32>(x, nslots, q, s, stream);
+  if (fmt == kScaleFloat32CeilUe8m0)
+    return launch_quant_t<32, kScaleFloat32CeilUe8m0>(x, nslots, q, s, stream);
+  return launch_quant_t<32, kScaleUe8m0>(x, nslots, q, s, stream);
+}
+
+hipError_t launch_group_quant(const void* x, long long M, int K, uint8_t* q, float* s,
+                              hipStream_t stream) {
+  return launch_group_quant_fmt(x, M, K, 128, kScaleFloat32, q, s, stream);
 }
 
 }  // namespace moe

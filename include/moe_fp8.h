@@ -169,6 +169,38 @@ int moe_fp8_forward_traced(const void* x, const float* router_logits,
 int per_token_group_quant_fp8(const void* x, int M, int K, int group_size,
                               uint8_t* q, float* scales, hipStream_t stream);
 
+/* Scale formats of per_token_group_quant_fp8_fmt (overview page, "DeepGEMM
+ * Scale Formats"). */
+typedef enum {
+  MOE_SCALE_FLOAT32 = 0,            /* float32 s = max(amax, 1e-8) / 448 */
+  MOE_SCALE_FLOAT32_CEIL_UE8M0 = 1, /* float32, that s rounded up to a power of two */
+  MOE_SCALE_UE8M0 = 2               /* uint8 exponent byte e of that power: s = 2^(e - 127) */
+} moe_scale_format;
+
+/*
+ * Per-token-group FP8 quantisation with a choice of group size and scale
+ * format: the float32 scales of per_token_group_quant_fp8, the same scales
+ * rounded up to a power of two (FLOAT32_CEIL_UE8M0 of the overview page's
+ * "DeepGEMM Scale Formats"), or their UE8M0 exponent bytes (UE8M0 there; with
+ * group 32 the MXFP8 [1, 32] activation quant of the fp8 oracle API page,
+ * whose scales are uint8 UE8M0 values laid out [num_tokens, hidden / 32]).
+ *   s32[m, g]  = max(max_i |x[m, G*g + i]|, 1e-8) / 448           (float32, RNE)
+ *   s[m, g]    = s32 (FLOAT32) or the smallest power of two >= s32 (the others)
+ *   q[m, k]    = e4m3fn_RNE_saturate(x[m, k] / s[m, k / G])      (float32 quotient;
+ *                exact for a power-of-two s, and then never saturating)
+ *   scales     float32 [M, K / G] holding s, or for MOE_SCALE_UE8M0 uint8
+ *              [M, K / G] holding log2(s) + 127.  Row-major bytes are the
+ *              "four per int32" packing read as little-endian int32 words
+ *              (group 4w + i in byte i of word w) when K / G is a multiple of 4.
+ *
+ *   x  bf16 [M, K] (16-byte aligned); q e4m3fn [M, K] (8-byte aligned)
+ *   group_size G is 32 or 128 (else MOE_ERR_UNSUPPORTED); K a positive
+ *   multiple of G; M >= 0 (M == 0 enqueues nothing); scale_format a
+ *   moe_scale_format (else MOE_ERR_UNSUPPORTED).
+ */
+int per_token_group_quant_fp8_fmt(const void* x, int M, int K, int group_size, int scale_format,
+                                  uint8_t* q, void* scales, hipStream_t stream);
+
 /*
  * Router stage alone (the top-K router of the overview page's "FusedMoE
  * Class"): softmax over E logits, the top_k experts by logit (ties to the

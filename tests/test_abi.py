@@ -121,6 +121,15 @@ def test_stage_argument_checks():
     assert lib.per_token_group_quant_fp8(None, 0, 256, 128, None, None, None) == 0   # empty: no-op
     assert lib.per_token_group_quant_fp8(None, 4, 256, 128, vp(4096), vp(8192), None) == -1
     assert lib.per_token_group_quant_fp8(vp(0x10000), 4, 256, 128, vp(0x10000 + 128), vp(1 << 30), None) == -6
+    f = lib.per_token_group_quant_fp8_fmt
+    assert f(vp(16), 4, 256, 64, 2, vp(4096), vp(8192), None) == -3           # group 64
+    assert f(vp(16), 4, 256, 32, 3, vp(4096), vp(8192), None) == -3           # format 3
+    assert f(vp(16), 4, 48, 32, 2, vp(4096), vp(8192), None) == -2            # K % 32
+    assert f(vp(16), 4, 160, 128, 1, vp(4096), vp(8192), None) == -2          # K % 128
+    assert f(None, 0, 256, 32, 2, None, None, None) == 0                      # empty: no-op
+    assert f(vp(16), 4, 256, 32, 2, None, vp(8192), None) == -1
+    assert f(vp(16), 4, 256, 32, 1, vp(4096), vp(8194), None) == -3           # float scales misaligned
+    assert f(vp(0x10000), 4, 256, 32, 2, vp(1 << 20), vp(0x10000 + 2047), None) == -6  # scales in x
     assert lib.moe_topk_softmax(vp(16), 4, 8, 9, 1, vp(64), vp(128), None) == -2
     assert lib.moe_topk_softmax(vp(16), 4, 600, 2, 1, vp(64), vp(128), None) == -2
     assert lib.moe_topk_softmax(None, 4, 8, 2, 1, vp(64), vp(128), None) == -1

@@ -83,6 +83,75 @@ def test_quant_full_size_workload():
     assert np.array_equal(np_(q)[rows], rq)
 
 
+FMTS = [(g, f) for g in (32, 128) for f in ("float32", "float32_ceil_ue8m0", "ue8m0")]
+
+
+def _quant_fmt_check(x_bf16, group, fmt, rows=None):
+    q, s = moe.per_token_group_quant_fp8_fmt(x_bf16.cuda(), group, fmt)
+    torch.cuda.synchronize()
+    xf = x_bf16.float().cpu().numpy()
+    qg, sg = np_(q), np_(s)
+    if rows is not None:
+        xf, qg, sg = xf[rows], qg[rows], sg[rows]
+    if fmt == "float32":
+        rq, rs = ref_quant.per_token_group_quant(xf, group)
+    else:
+        rq, rs, rex = ref_quant.per_token_group_quant_pow2(xf, group)
+        if fmt == "ue8m0":
+            rs = rex
+    assert sg.dtype == rs.dtype and np.array_equal(sg.view(np.uint8), rs.view(np.uint8)), "scales differ"
+    bad = np.nonzero(qg != rq)
+    assert bad[0].size == 0, f"{bad[0].size} codes differ, first at {bad[0][0]},{bad[1][0]}"
+
+
+@pytest.mark.parametrize("group,fmt", FMTS)
+@pytest.mark.parametrize("M,K", [(1, 128), (37, 384), (301, 7168), (3, 32 * 7 + 96)])
+def test_quant_fmt_random_with_outliers(group, fmt, M, K):
+    if K % group:
+        pytest.skip("K not a multiple of the group")
+    note(f"quant fmt={fmt} group={group} M={M} K={K}")
+    _quant_fmt_check(quant_input(M, K, seed_base=M * 11 + K + group), group, fmt)
+
+
+@pytest.mark.parametrize("group,fmt", FMTS)
+def test_quant_fmt_special_groups(group, fmt):
+    """Scales at and beside exact powers of two (amax = 448 * 2^k, one bf16
+    step either side), negative zeros, values under the amax clamp, bf16
+    subnormals and the largest bf16 magnitudes."""
+    note(f"quant fmt={fmt} group={group} special groups")
+    rows = []
+    for k in range(-20, 21, 5):
+        for step in (-1, 0, 1):
+            bits = np.array([448.0 * 2.0 ** k], np.float32).view(np.uint32).astype(np.int64) + (step << 16)
+            a = bits.astype(np.uint32).view(np.float32)[0]
+            r = np.random.default_rng(100 + k * 3 + step).uniform(-a, a, 2 * group).astype(np.float32)
+            r[0], r[group + 1] = a, -a
+            rows.append(r)
+    x = np.stack(rows)
+    z = np.zeros((5, 2 * group), np.float32)
+    z[0, :group] = -0.0
+    z[1] = 1e-30
+    z[2] = np.float32(2.0 ** -130)
+    z[3] = 3.0e38
+    z[3, 1::2] = -1.5
+    z[4, 0] = 1e4
+    z[4, 1:] = 1.0
+    x = np.concatenate([x, z])
+    _quant_fmt_check(torch.from_numpy(x).to(torch.bfloat16), group, fmt)
+
+
+@pytest.mark.parametrize("group,fmt", [(32, "ue8m0"), (128, "float32_ceil_ue8m0")])
+def test_quant_fmt_full_size_workload(group, fmt):
+    """bf16 [16384, 7168] with 1% outliers in the launch configuration the
+    benchmark times; codes and scales bit-exact on 1024 sampled rows plus the
+    first and last."""
+    M = QUANT_WORKLOAD["M"]
+    note(f"quant fmt={fmt} group={group} full size")
+    x = quant_input(device="cuda")
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(1).choice(M, 1024, replace=False)]))
+    _quant_fmt_check(x, group, fmt, rows=rows)
+
+
 @pytest.mark.parametrize("T,E,k,renorm,kind", [
     (16, 8, 2, True, "normal"), (64, 256, 8, True, "bias"), (33, 128, 8, False, "normal"),
     (1, 128, 8, True, "normal"), (7, 5, 5, True, "normal"), (3, 1, 1, False, "normal"),

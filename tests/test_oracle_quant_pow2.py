@@ -94,3 +94,13 @@ def test_planted_round_down_fails():
     q, s, _ = quant.per_token_group_quant_pow2(x, 128)
     codes, p = _brute_group(x[0], round_down=True)
     assert s[0, 0] != p or list(q[0]) != codes
+
+
+def test_float32_scales_group_32_brute_force():
+    # the float32-scale quantiser at group 32 (the other formats' float32 s)
+    x = quant_input(M=2, K=128, seed_base=61).float().numpy()
+    q, s = quant.per_token_group_quant(x, 32)
+    for r in range(2):
+        for g in range(4):
+            codes, sc = _brute.quant_group_scalar(x[r, 32 * g:32 * (g + 1)])
+            assert list(q[r, 32 * g:32 * (g + 1)]) == codes and s[r, g] == sc
