@@ -15,16 +15,28 @@ w_scale [N/128, K/128]:
 Applying the two scales per 128-wide K block to each block's partial sum
 (the kernels' order) is the same sum up to rounding order.
 
+The MXFP8 linear (mxfp8_linear): fp8 oracle API page, the MXFP8 block shape
+[1, 32] with uint8 UE8M0 activation scales [num_tokens, hidden / 32], and
+the overview page's "DeepGEMM Scale Formats" (power-of-two scales as UE8M0
+exponent bytes).  Both operands carry one power-of-two scale per row and 32
+consecutive K elements:
+  1. (xq, xs, xe) = quant.per_token_group_quant_pow2(x, 32)
+     Xf[m, k] = dec(xq[m, k]) * 2^(xe[m, k/32] - 127)   (float64)
+  2. Wf[n, k] = dec(w[n, k]) * 2^(w_e[n, k/32] - 127)   (float64)
+  3. out = bf16_RNE(Xf @ Wf^T)
+
 Parity: pinned in tests/test_oracle_linear.py by a brute force with explicit
 per-K-block scale indexing, a closed form (unit scales and e4m3-exact
 activations give an exact integer product), row-permutation equivariance,
 the effect of scaling the weight scales, and a loose match to the
-unquantised float64 product.
+unquantised float64 product; the MXFP8 form by a scalar brute force over
+32-wide blocks with planted mistakes (a 128-wide scale block, transposed
+exponent indexing), exponent covariance and the unquantised product.
 """
 
 import numpy as np
 
-from . import quant
+from . import e4m3, quant
 from .moe import bf16_round
 
 
@@ -38,3 +50,23 @@ def block_fp8_linear(x, w, w_scale):
     Wf = quant.block_dequant(w, w_scale)
     acc = Xf @ Wf.T
     return bf16_round(acc), {"xq": xq, "xs": xs, "acc": acc}
+
+
+def mx_dequant(q, e, block: int = 32) -> np.ndarray:
+    """uint8 codes [R, K], UE8M0 exponent bytes [R, K/block] -> float64
+    [R, K] with value dec(q[r, k]) * 2^(e[r, k // block] - 127)."""
+    q = np.asarray(q, dtype=np.uint8)
+    R, K = q.shape
+    d = e4m3.decode(q).reshape(R, K // block, block)
+    p = np.ldexp(1.0, np.asarray(e, dtype=np.int64) - 127)
+    return (d * p[:, :, None]).reshape(R, K)
+
+
+def mxfp8_linear(x, w, w_e):
+    """x float32 [M, K] holding bf16 values, w uint8 [N, K], w_e uint8
+    [N, K/32].  Returns (out float32 [M, N] holding bf16 values, info with xq,
+    xe and the float64 product before rounding)."""
+    x = np.asarray(x, dtype=np.float32)
+    xq, _, xe = quant.per_token_group_quant_pow2(x, 32)
+    acc = mx_dequant(xq, xe) @ mx_dequant(w, w_e).T
+    return bf16_round(acc), {"xq": xq, "xe": xe, "acc": acc}

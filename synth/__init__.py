@@ -39,6 +39,9 @@ QUANT_WORKLOAD = dict(index=4, M=16384, K=7168, outlier_frac=0.01, outlier_mul=1
 # Dense block-FP8 linear: a DeepSeek-V3-shaped dense down projection
 # (out features 7168, in features 18432) at a decode and a prefill batch
 LINEAR_WORKLOAD = dict(index=5, N=7168, K=18432, M=(64, 8192))
+# The same dense shape with MXFP8 operands: [1, 32] blocks, UE8M0 scales
+MX_LINEAR_WORKLOAD = dict(index=6, N=7168, K=18432, M=(64, 8192))
+MX_BLOCK = 32
 
 WEIGHT_STD = 0.02
 BLOCK = 128
@@ -59,6 +62,21 @@ def block_quantize_e4m3(w: torch.Tensor):
     scale = (amax / 448.0).to(torch.float32)
     q = (b / scale[:, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
     return q.view(torch.uint8).reshape(N, K).contiguous(), scale.contiguous()
+
+
+def mx_quantize_e4m3(w: torch.Tensor):
+    """float32 [N, K] -> (uint8 e4m3fn codes [N, K], uint8 UE8M0 exponents
+    [N, K/32]): a checkpoint stand-in with one power-of-two scale per row and
+    32 consecutive columns, the block amax / 448 rounded up to a power of two
+    (torch.frexp), and torch's float8 cast of w / scale."""
+    N, K = w.shape
+    b = w.reshape(N, K // MX_BLOCK, MX_BLOCK)
+    amax = b.abs().amax(dim=2).clamp_min(1e-8)
+    m, ex = torch.frexp((amax / 448.0).to(torch.float32))
+    ex = ex - (m == 0.5).to(ex.dtype)                  # 2^ex >= amax / 448, the least such
+    scale = torch.ldexp(torch.ones_like(amax), ex)
+    q = (b / scale[:, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).reshape(N, K).contiguous(), (ex + 127).to(torch.uint8).contiguous()
 
 
 def make_weights(H, I, E, seed, device="cpu", std=WEIGHT_STD):
@@ -137,3 +155,17 @@ def make_linear(M, N, K, seed_base, device="cpu", std=WEIGHT_STD):
                     dtype=torch.float32) * std
     wq, ws = block_quantize_e4m3(w)
     return x, wq, ws
+
+
+def make_mx_linear(M, N, K, seed_base, device="cpu", std=WEIGHT_STD):
+    """MXFP8 dense linear inputs: x bf16 [M, K] ~ N(0, 1) (seed_base + 0) and
+    a weight [N, K] ~ N(0, std) (seed_base + 2) as e4m3fn codes [N, K] with
+    UE8M0 exponent bytes [N, K/32]."""
+    if N % 128 or K % 128:
+        raise ValueError("N and K must be multiples of 128")
+    x = torch.randn((M, K), generator=_gen(device, seed_base + 0), device=device,
+                    dtype=torch.float32).to(torch.bfloat16).contiguous()
+    w = torch.randn((N, K), generator=_gen(device, seed_base + 2), device=device,
+                    dtype=torch.float32) * std
+    wq, we = mx_quantize_e4m3(w)
+    return x, wq, we
