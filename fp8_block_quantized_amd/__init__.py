@@ -30,7 +30,8 @@ EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layo
            "moe_fp8_forward", "moe_fp8_forward_traced", "per_token_group_quant_fp8",
            "per_token_group_quant_fp8_fmt", "moe_topk_softmax",
            "moe_align_scratch_bytes", "moe_align", "moe_status_string",
-           "fp8_block_linear_workspace_bytes", "fp8_block_linear"]
+           "fp8_block_linear_workspace_bytes", "fp8_block_linear",
+           "mxfp8_linear_workspace_bytes", "mxfp8_linear"]
 
 
 class MoeError(RuntimeError):
@@ -76,6 +77,10 @@ def load_library(path=LIB_PATH):
     lib.fp8_block_linear_workspace_bytes.restype = c_size
     lib.fp8_block_linear.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, vp, c_size, vp]
     lib.fp8_block_linear.restype = c_int
+    lib.mxfp8_linear_workspace_bytes.argtypes = [c_int] * 3
+    lib.mxfp8_linear_workspace_bytes.restype = c_size
+    lib.mxfp8_linear.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, vp, c_size, vp]
+    lib.mxfp8_linear.restype = c_int
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -279,4 +284,29 @@ def fp8_block_linear(x, w, w_scale, out=None, workspace=None, stream=None):
         M, N, K, _dev(out, torch.bfloat16, "out"), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream))
     _check("fp8_block_linear", st)
+    return out
+
+
+def mxfp8_linear_workspace_bytes(M, N, K):
+    return load_library().mxfp8_linear_workspace_bytes(M, N, K)
+
+
+def mxfp8_linear(x, w, w_scale, out=None, workspace=None, stream=None):
+    """MXFP8 dense linear: x bf16 [M, K], w uint8 e4m3fn [N, K], w_scale uint8
+    UE8M0 exponents [N, K/32] -> out bf16 [M, N] (x quantised per 32-group of
+    each row with power-of-two scales)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        n = mxfp8_linear_workspace_bytes(M, N, K)
+        if n == 0:
+            raise MoeError("mxfp8_linear_workspace_bytes", -2)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    st = load_library().mxfp8_linear(
+        _dev(x, torch.bfloat16, "x"), _dev(w, torch.uint8, "w"), _dev(w_scale, torch.uint8, "w_scale"),
+        M, N, K, _dev(out, torch.bfloat16, "out"), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check("mxfp8_linear", st)
     return out

@@ -67,6 +67,8 @@ struct GemmArgs {
   uint16_t* y_dump;          // GEMM2: 1024 bytes
   int ksplit;                // GEMM2 prefill: K slices per tile (1: bf16 y_out)
   float* part;               // GEMM2, ksplit > 1: float32 partials [ksplit, y_rows, y_stride]
+  int mx;                    // GEMM2 prefill: act_scale and w_scale hold UE8M0 exponent bytes,
+                             // one per row and 32 K elements ([rows, K/32] and [E, N, K/32])
 };
 
 // M0 is written only inside these statements, each right before its load;
@@ -533,6 +535,17 @@ constexpr int kRingW = 256 * 128;      // 256 weight rows x one 128-byte K block
 // Needs at least two K blocks per tile.  A tile may cover one of ksplit equal
 // K slices (for outputs with few tiles): it then stores float32 partials,
 // which a reduction kernel sums in slice order.
+//
+// kMx: both operands carry a power-of-two scale per row and 32 K elements
+// (MXFP8), applied by the MFMA itself (v_mfma_scale_f32_16x16x128_f8f6f4):
+// the lane that holds 32 K values of a row in the instruction's K order
+// (bytes 16g..16g+15 and 64+16g..64+16g+15 of the block for lane group g)
+// passes the exponent byte of that row's 32-element block g, so the scale
+// blocks of the instruction are exactly the 32-wide blocks of memory.  The
+// accumulator then runs through the MFMAs across K blocks with no float
+// fold.  The stage holds the exponent words of the 128 token rows (as the
+// float scales would) and of the tile's 256 weight rows, loaded by waves 2-5
+// in the slots the other waves leave unused.
 constexpr int kPf2Loads = 7;               // DMA instructions per wave per stage
 constexpr int kPf2Stores = 16;             // output stores per wave per tile
 constexpr int kPf2S = 2048;                // token scales, eight 256-byte wave slots
@@ -542,8 +555,15 @@ struct TileId {
 };
 
 // Logical tile L -> (expert, m block, n tile) in expert-major order, by a
-// binary search over the expert block offsets.  Scalar loads only: they stay
-// out of the vector memory counter that the ring's waits rely on.
+// binary search over the expert block offsets.  Within an expert the row
+// blocks go in groups of kRowGroup: group-major, then n tile, then the
+// group's row blocks.  The 32 workgroups of an XCD that run together then
+// cover 8 row blocks x 4 weight panels (256 KB of operands per K block from
+// beyond L2) rather than 32 row blocks x 1 panel (544 KB); an expert with at
+// most 8 row blocks is one group.  Scalar loads only: they stay out of the
+// vector memory counter that the ring's waits rely on.
+constexpr int kRowGroup = 8;
+
 __device__ __forceinline__ TileId tile_id(int L, const GemmArgs& a, int ksplit) {
   const int ks = L % ksplit;
   L /= ksplit;
@@ -554,11 +574,14 @@ __device__ __forceinline__ TileId tile_id(int L, const GemmArgs& a, int ksplit) 
     if (load_uniform(a.eoff + mid) * nt <= L) lo = mid; else hi = mid - 1;
   }
   const int b0 = load_uniform(a.eoff + lo), nb = load_uniform(a.eoff + lo + 1) - b0;
-  const int local = L - b0 * nt, j = local / nb;
-  return {lo, b0 + (local - j * nb), j, ks};
+  const int local = L - b0 * nt;
+  const int grp = local / (kRowGroup * nt), rem = local - grp * kRowGroup * nt;
+  const int left = nb - grp * kRowGroup, gb = left < kRowGroup ? left : kRowGroup;
+  const int j = rem / gb;
+  return {lo, b0 + grp * kRowGroup + (rem - j * gb), j, ks};
 }
 
-template <bool kSplitK>
+template <bool kSplitK, bool kMx>
 __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   constexpr int BM = 128;
   constexpr int kA = BM * 128, kStage = kRingW + kA + kPf2S;
@@ -606,7 +629,14 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
     for (int i = 0; i < 4; ++i) dma16s(wo[i], wb, base + (wave * 4 + i) * 1024);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16s(aoff[i], ab, base + kRingW + (wave * 2 + i) * 1024);
-    dma4s(soff, sb, base + kRingW + kA + wave * 256);
+    if (kMx && wave >= 2 && wave < 6) {
+      // exponent words of weight rows 256 j + 64 (wave - 2) + lane at K block kg
+      const int row = 256 * t.j + 64 * (wave - 2) + lane;
+      const uint8_t* eb = (const uint8_t*)args.w_scale + ((size_t)t.e * N * nkb + kg) * 4;
+      dma4s((uint32_t)((row < N ? row : 0) * nkb * 4), eb, base + kRingW + kA + wave * 256);
+    } else {
+      dma4s(soff, sb, base + kRingW + kA + wave * 256);
+    }
   };
   // LDS byte offsets of this lane's operand pieces: row, chunks g and g + 4;
   // rows 16 apart share the swizzle, so each fragment is a base + immediate
@@ -630,7 +660,8 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   int s = 0;
   for (int ti = 0; ti < ntile; ++ti) {
     const int nf = 256 * cur.j + 64 * wf;
-    const float* wsp = args.w_scale + ((size_t)cur.e * (N >> 7) + ((nf < N ? nf : 0) >> 7)) * nkb;
+    const float* wsp = kMx ? nullptr
+                           : args.w_scale + ((size_t)cur.e * (N >> 7) + ((nf < N ? nf : 0) >> 7)) * nkb;
     v4f acc[4][4];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
@@ -649,7 +680,6 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
         else issue((s + 2) % kRingStages, nxt, nwo, kb + 2 - nkb_t);
       }
       const uint8_t* st = ring + (s % kRingStages) * kStage;
-      const float sw = load_uniform(wsp + cur.ks * nkb_t + kb);
       v8i pf[4];
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
@@ -657,17 +687,38 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
         const uint4 a1 = *(const uint4*)(st + pbase[1] + pp * 2048);
         pf[pp] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       }
+      if (kMx) {
+        // exponent bytes: weight row 64 wf + 16 pp + l16 at stage byte 512 + 4 row + g,
+        // token row 64 wt + 16 q + l16 at 4 row + g
+        const uint8_t* se = st + kRingW + kA;
+        int ew[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 b0 = *(const uint4*)(st + qbase[0] + q * 2048);
-        const uint4 b1 = *(const uint4*)(st + qbase[1] + q * 2048);
-        const v8i bq = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        const float sc = *(const float*)(st + kRingW + kA + (64 * wt + 16 * q + l16) * 4) * sw;
+        for (int pp = 0; pp < 4; ++pp) ew[pp] = se[512 + (64 * wf + 16 * pp + l16) * 4 + g];
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf[pp], bq, zero, 0, 0, 0, 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const uint4 b0 = *(const uint4*)(st + qbase[0] + q * 2048);
+          const uint4 b1 = *(const uint4*)(st + qbase[1] + q * 2048);
+          const v8i bq = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          const int ea = se[(64 * wt + 16 * q + l16) * 4 + g];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
+          for (int pp = 0; pp < 4; ++pp)
+            acc[pp][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf[pp], bq, acc[pp][q], 0, 0,
+                                                                         0, ew[pp], 0, ea);
+        }
+      } else {
+        const float sw = load_uniform(wsp + cur.ks * nkb_t + kb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 b0 = *(const uint4*)(st + qbase[0] + q * 2048);
+          const uint4 b1 = *(const uint4*)(st + qbase[1] + q * 2048);
+          const v8i bq = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          const float sc = *(const float*)(st + kRingW + kA + (64 * wt + 16 * q + l16) * 4) * sw;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf[pp], bq, zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
+          }
         }
       }
     }
@@ -913,7 +964,9 @@ static hipError_t launch_reduce_slices(const float* part, int ksplit, int rows, 
 
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
-  if (BM == 128 && (a.K >> 7) / a.ksplit >= 2) {
+  const bool persistent = BM == 128 && (a.K >> 7) / a.ksplit >= 2;
+  if (a.mx && !persistent) return hipErrorInvalidValue;     // exponent scales: persistent kernel only
+  if (persistent) {
     // one persistent workgroup per CU, a multiple of the 8 XCDs
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -923,10 +976,14 @@ static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream)
     long long wg = cus / 8 * 8;
     if (wg > (tiles + 7) / 8 * 8) wg = (tiles + 7) / 8 * 8;
     if (wg < 8) wg = 8;
-    if (a.ksplit > 1)
-      hipLaunchKernelGGL(moe_gemm2_pf_kernel<true>, dim3((unsigned)wg), dim3(512), 0, stream, a);
+    if (a.mx && a.ksplit > 1)
+      hipLaunchKernelGGL((moe_gemm2_pf_kernel<true, true>), dim3((unsigned)wg), dim3(512), 0, stream, a);
+    else if (a.mx)
+      hipLaunchKernelGGL((moe_gemm2_pf_kernel<false, true>), dim3((unsigned)wg), dim3(512), 0, stream, a);
+    else if (a.ksplit > 1)
+      hipLaunchKernelGGL((moe_gemm2_pf_kernel<true, false>), dim3((unsigned)wg), dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(moe_gemm2_pf_kernel<false>, dim3((unsigned)wg), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((moe_gemm2_pf_kernel<false, false>), dim3((unsigned)wg), dim3(512), 0, stream, a);
     return hipGetLastError();
   }
   switch (BM) {
@@ -989,8 +1046,9 @@ hipError_t launch_gemm2_bounded(const uint8_t* act, const float* act_scale, cons
                                 const int32_t* expert_ids, const int32_t* ntpp, const int32_t* eoff,
                                 int N, int K, int P, int BM, int nblk, uint16_t* y, int y_stride,
                                 int y_rows, int y_cols, uint16_t* y_dump, int ksplit, float* part,
-                                hipStream_t stream) {
+                                bool mx, hipStream_t stream) {
   GemmArgs a{};
+  a.mx = mx ? 1 : 0;
   a.eoff = eoff; a.E = 1; a.split = 1;
   a.act = act; a.act_scale = act_scale; a.w = w; a.w_scale = w_scale;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;

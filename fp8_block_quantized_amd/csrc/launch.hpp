@@ -34,13 +34,15 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
                         uint16_t* y, int y_stride, hipStream_t stream);
 // GEMM2 with an output bounded to rows [0, y_rows) and columns [0, y_cols):
 // stores outside go to a 1024-byte dump; with ksplit > 1, K slices go to
-// float32 partials [ksplit, y_rows, y_cols] and are summed into y (the dense linear)
+// float32 partials [ksplit, y_rows, y_cols] and are summed into y (the dense linear).
+// mx: act_scale / w_scale point at UE8M0 exponent bytes, one per row and 32 K
+// elements (BM must be 128 and every K slice at least two 128-blocks)
 hipError_t launch_gemm2_bounded(const uint8_t* act, const float* act_scale, const uint8_t* w,
                                 const float* w_scale, const int32_t* sorted_ids,
                                 const int32_t* expert_ids, const int32_t* ntpp, const int32_t* eoff,
                                 int N, int K, int P, int BM, int nblk, uint16_t* y, int y_stride,
                                 int y_rows, int y_cols, uint16_t* y_dump, int ksplit, float* part,
-                                hipStream_t stream);
+                                bool mx, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* y, int y_stride, const int32_t* pair_pos,
                           const float* topk_w, int T, int H, int top_k, uint16_t* out,
                           hipStream_t stream);

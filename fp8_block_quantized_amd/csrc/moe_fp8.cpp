@@ -366,7 +366,52 @@ int fp8_block_linear(const void* x, const uint8_t* w, const float* w_scale, int 
   if (moe::launch_group_quant(x, M, K, xq, xs, stream)) return MOE_ERR_HIP;
   if (moe::launch_identity_layout(M, L.BM, L.nblk, sorted, eids, eoff, ntpp, stream)) return MOE_ERR_HIP;
   if (moe::launch_gemm2_bounded(xq, xs, w, w_scale, sorted, eids, ntpp, eoff, N, K, M, L.BM, L.nblk,
-                                (uint16_t*)out, N, M, N, dump, L.ksplit, part, stream))
+                                (uint16_t*)out, N, M, N, dump, L.ksplit, part, false, stream))
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+// The MXFP8 linear reuses the dense layout: the activation scale region holds
+// cap * K/128 floats, i.e. exactly the cap * K/32 exponent bytes.
+size_t mxfp8_linear_workspace_bytes(int M, int N, int K) {
+  if (check_linear_shape(M, N, K) != MOE_OK || K < 256) return 0;
+  LinearLayout L;
+  make_linear_layout(M, N, K, L);
+  return L.total;
+}
+
+int mxfp8_linear(const void* x, const uint8_t* w, const uint8_t* w_scale, int M, int N, int K,
+                 void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_linear_shape(M, N, K);
+  if (st != MOE_OK) return st;
+  if (K < 256) return MOE_ERR_UNSUPPORTED;
+  if (!x || !w || !w_scale || !out || !workspace) return MOE_ERR_NULL;
+  if ((uintptr_t)x % 16 || (uintptr_t)w % 16 || (uintptr_t)w_scale % 4 || (uintptr_t)out % 16 ||
+      (uintptr_t)workspace % kAlign)
+    return MOE_ERR_UNSUPPORTED;
+  LinearLayout L;
+  make_linear_layout(M, N, K, L);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const size_t xb = (size_t)M * K * 2, ob = (size_t)M * N * 2;
+  const size_t wb = (size_t)N * K, sb = (size_t)N * (K / 32);
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || overlaps(out, ob, w_scale, sb) ||
+      overlaps(workspace, L.total, x, xb) || overlaps(workspace, L.total, w, wb) ||
+      overlaps(workspace, L.total, w_scale, sb) || overlaps(workspace, L.total, out, ob))
+    return MOE_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  uint8_t* xq = (uint8_t*)(ws + L.xq);
+  uint8_t* xe = (uint8_t*)(ws + L.xs);
+  int32_t* sorted = (int32_t*)(ws + L.sorted);
+  int32_t* eids = (int32_t*)(ws + L.eids);
+  int32_t* eoff = (int32_t*)(ws + L.meta);
+  int32_t* ntpp = eoff + 2;
+  uint16_t* dump = (uint16_t*)(ws + L.dump);
+  float* part = (float*)(ws + L.part);
+  if (moe::launch_group_quant_fmt(x, M, K, 32, moe::kScaleUe8m0, xq, xe, stream)) return MOE_ERR_HIP;
+  if (moe::launch_identity_layout(M, L.BM, L.nblk, sorted, eids, eoff, ntpp, stream)) return MOE_ERR_HIP;
+  if (moe::launch_gemm2_bounded(xq, (const float*)xe, w, (const float*)w_scale, sorted, eids, ntpp,
+                                eoff, N, K, M, L.BM, L.nblk, (uint16_t*)out, N, M, N, dump,
+                                L.ksplit, part, true, stream))
     return MOE_ERR_HIP;
   return MOE_OK;
 }

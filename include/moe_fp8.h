@@ -234,7 +234,6 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
               int32_t* num_tokens_post_padded,
               void* scratch, size_t scratch_bytes, hipStream_t stream);
 
-/* Static description of a moe_status code. */
 /*
  * Dense block-FP8 linear layer (overview page, "W8A8BlockFp8LinearOp - Block
  * FP8 GEMM Dispatch": the block-wise FP8 GEMM of DeepSeek-V3-style dense
@@ -262,6 +261,32 @@ size_t fp8_block_linear_workspace_bytes(int M, int N, int K);
 int fp8_block_linear(const void* x, const uint8_t* w, const float* w_scale, int M, int N, int K,
                      void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * MXFP8 dense linear layer: the block shape [1, 32] of the fp8 oracle API
+ * page (activations quantised by the MXFP8 activation quant, uint8 UE8M0
+ * scales [num_tokens, hidden / 32]), with the weight in the same format (an
+ * MXFP8 checkpoint: e4m3fn codes and one UE8M0 exponent byte per row and 32
+ * K elements; overview page, "DeepGEMM Scale Formats", UE8M0):
+ *   (xq, xe) = per_token_group_quant_fp8_fmt(x, group 32, MOE_SCALE_UE8M0)
+ *   out[m, n] = bf16_RNE( sum_k dec(xq[m, k]) * 2^(xe[m, k/32] - 127)
+ *                               * dec(w[n, k]) * 2^(w_scale[n, k/32] - 127) )
+ * accumulated in float32 by FP8 MFMAs that apply both exponents in hardware.
+ *
+ *   x        bf16    [M, K]          device, 16-byte aligned
+ *   w        e4m3fn  [N, K]          device, 16-byte aligned, one output per row
+ *   w_scale  uint8   [N, K/32]       device, 4-byte aligned, UE8M0 bytes (255 is NaN)
+ *   out      bf16    [M, N]          device, must not overlap any input
+ *   workspace: mxfp8_linear_workspace_bytes(M, N, K) bytes, 256-byte aligned,
+ *   caller-owned, contents undefined on return.
+ * Constraints: those of fp8_block_linear, and K >= 256 (K == 128 returns
+ * MOE_ERR_UNSUPPORTED; the workspace query returns 0).  Returns MOE_OK or a
+ * negative moe_status (checked before anything is enqueued).
+ */
+size_t mxfp8_linear_workspace_bytes(int M, int N, int K);
+int mxfp8_linear(const void* x, const uint8_t* w, const uint8_t* w_scale, int M, int N, int K,
+                 void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a moe_status code. */
 const char* moe_status_string(int status);
 
 #ifdef __cplusplus

@@ -175,3 +175,29 @@ def test_linear_workspace_and_argument_checks():
     assert call(*bad) == -6                      # out overlaps x
     bad = list(ok); bad[7] = vp(0x7000000000 + 8)
     assert call(*bad) == -3                      # workspace misaligned
+
+
+def test_mx_linear_workspace_and_argument_checks():
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    M, N, K = 64, 256, 512
+    need = moe.mxfp8_linear_workspace_bytes(M, N, K)
+    assert need == moe.fp8_block_linear_workspace_bytes(M, N, K) > 0
+    assert moe.mxfp8_linear_workspace_bytes(M, N, 128) == 0             # one K block
+    assert moe.mxfp8_linear_workspace_bytes(M, N + 64, K) == 0
+    x, w, s, out = (vp(0x10000 * i) for i in (1, 2, 3, 4))
+    ws = vp(0x7000000000)
+    f = lib.mxfp8_linear
+    ok = [x, w, s, M, N, K, out, ws, need, None]
+    bad = list(ok); bad[5] = 128
+    assert f(*bad) == -3                         # K = 128 unsupported
+    bad = list(ok); bad[5] = 200
+    assert f(*bad) == -2
+    bad = list(ok); bad[2] = None
+    assert f(*bad) == -1
+    bad = list(ok); bad[8] = need - 1
+    assert f(*bad) == -4
+    bad = list(ok); bad[2] = vp(0x30002)
+    assert f(*bad) == -3                         # exponent bytes not 4-byte aligned
+    bad = list(ok); bad[6] = vp(0x30000 + 16)
+    assert f(*bad) == -6                         # out overlaps the exponents (N*K/32 bytes)

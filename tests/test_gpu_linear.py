@@ -1,15 +1,17 @@
 """GPU parity of the dense block-FP8 linear (fp8_block_linear through the C
-ABI) against oracle/linear.py.
+ABI) and the MXFP8 linear (mxfp8_linear) against oracle/linear.py.
 
 The activation quantiser is the forward's (its codes and scales are exact
 targets in tests/test_gpu_stages.py); the product runs on FP8 MFMAs with a
 float32 accumulator, whose rounding reaches the bf16 output smoothly, so the
 output bar is the layer's: |gpu - ref| <= 1e-2 + 2e-2 |ref| everywhere and a
-relative norm error below 1e-2.  The small cases cover every block size the
-library picks (16 to 128 rows), a ragged last block, an output width that is
-not a multiple of 256 (the stores past it go to the workspace's dump), two K
-blocks and a single one; a garbage-filled workspace must not change a bit of
-the output.  The full-size DeepSeek-V3-shaped projection is compared on
+relative norm error below 1e-2.  The small cases cover one and several
+128-row blocks, a ragged last block, an output width that is not a multiple
+of 256 (the stores past it go to the workspace's dump), K split into slices
+and not, two K blocks and a single one; a garbage-filled workspace must not
+change a bit of the output.  The MXFP8 cases add exponents drawn at random
+per 32-element block on both operands, so that a scale applied to the wrong
+block shows as a factor of a power of two.  The full-size DeepSeek-V3-shaped projection is compared on
 sampled rows (each output row depends only on its own input row)."""
 
 import numpy as np
@@ -18,7 +20,7 @@ import torch
 
 import fp8_block_quantized_amd as moe
 from oracle import linear as ref_linear
-from synth import LINEAR_WORKLOAD, make_linear
+from synth import LINEAR_WORKLOAD, MX_LINEAR_WORKLOAD, make_linear, make_mx_linear
 from tests.gpu_util import assert_out_close, note, np_
 
 pytestmark = pytest.mark.gpu
@@ -68,4 +70,71 @@ def test_linear_full_size(M):
     rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(M, min(M, 6), replace=False)]))
     ref, _ = ref_linear.block_fp8_linear(np_(x[torch.from_numpy(rows).cuda()].float()), np_(w), np_(ws))
     m = assert_out_close(np_(out.float())[rows], ref, f"linear full-size M={M}")
+    note(f"  sampled {rows.size} rows: max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e}")
+
+
+# ---- MXFP8 ----
+
+def _mx_spread(M, N, K, seed):
+    """x bf16 N(0, 1) with each 32-group scaled by 2^u, u in [-6, 6]; weight
+    codes from N(0, 112) cast to e4m3 and exponent bytes 115 + [-4, 4],
+    both drawn per 32-element block."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((M, K), generator=g)
+    x = x * torch.pow(2.0, torch.randint(-6, 7, (M, K // 32, 1), generator=g).float()).expand(M, K // 32, 32).reshape(M, K)
+    w = (torch.randn((N, K), generator=g) * 112.0).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    we = (115 + torch.randint(-4, 5, (N, K // 32), generator=g)).to(torch.uint8)
+    return x.to(torch.bfloat16).contiguous(), w.contiguous(), we.contiguous()
+
+
+def _mx_check(x, w, we, what):
+    out = moe.mxfp8_linear(x.cuda(), w.cuda(), we.cuda())
+    torch.cuda.synchronize()
+    ref, _ = ref_linear.mxfp8_linear(x.float().numpy(), w.numpy(), we.numpy())
+    m = assert_out_close(np_(out.float()), ref, what)
+    note(f"  max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e}")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 128, 256),      # one row, K split in two slices
+    (5, 256, 384),      # ragged block, three K blocks (no split)
+    (100, 1024, 512),   # K split in two slices
+    (300, 640, 256),    # N not a multiple of 256, two K blocks
+    (130, 256, 2048),   # two row blocks, K split
+])
+@pytest.mark.parametrize("kind", ["synth", "spread"])
+def test_mx_linear_small(M, N, K, kind):
+    note(f"mxfp8 linear {kind} M={M} N={N} K={K}")
+    if kind == "synth":
+        x, w, we = make_mx_linear(M, N, K, seed_base=M + N + K)
+    else:
+        x, w, we = _mx_spread(M, N, K, seed=M * 3 + N + K)
+    _mx_check(x, w, we, f"mxfp8 linear {kind} {M}x{N}x{K}")
+
+
+def test_mx_linear_workspace_contents_do_not_matter():
+    M, N, K = 300, 640, 256
+    x, w, we = make_mx_linear(M, N, K, seed_base=78)
+    xd, wd, wed = x.cuda(), w.cuda(), we.cuda()
+    n = moe.mxfp8_linear_workspace_bytes(M, N, K)
+    clean = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    dirty = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN codes and NaN exponents
+    note("mxfp8 linear workspace garbage")
+    a = moe.mxfp8_linear(xd, wd, wed, workspace=clean)
+    b = moe.mxfp8_linear(xd, wd, wed, workspace=dirty)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.isfinite(a.float()).all()
+
+
+@pytest.mark.parametrize("M", MX_LINEAR_WORKLOAD["M"])
+def test_mx_linear_full_size(M):
+    N, K = MX_LINEAR_WORKLOAD["N"], MX_LINEAR_WORKLOAD["K"]
+    x, w, we = make_mx_linear(M, N, K, 1000 * MX_LINEAR_WORKLOAD["index"], device="cuda")
+    note(f"mxfp8 linear full-size M={M} N={N} K={K}")
+    out = moe.mxfp8_linear(x, w, we)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M + 1).choice(M, min(M, 6), replace=False)]))
+    ref, _ = ref_linear.mxfp8_linear(np_(x[torch.from_numpy(rows).cuda()].float()), np_(w), np_(we))
+    m = assert_out_close(np_(out.float())[rows], ref, f"mxfp8 linear full-size M={M}")
     note(f"  sampled {rows.size} rows: max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e}")
