@@ -39,12 +39,12 @@ STAGE_PEAK = {"gemm1": MFMA_F16_PEAK, "gemm2": MFMA_FP8_PEAK}
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
 # kernel source they were taken on: bench reports null traffic once
 # gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "6d7a0b8cec67f9becd8fb3ec5779182a3c8198d2e5ce0a0166ed37f1803c81db"
+TRAFFIC_SOURCE_SHA256 = "c87e73ea881b192fe9a1f7c0b97d8057bb123a91ef3cd9c98831ea90e842dd18"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
-    "prefill.gemm1": (8866457685, 181931029),
-    "prefill.gemm2": (4463134208, 1207437835),
-    "decode.gemm1": (4796014592, 5720363),
-    "decode.gemm2": (2408647893, 7340373),
+    "prefill.gemm1": (8866069823, 181941227),
+    "prefill.gemm2": (4460599191, 1207437397),
+    "decode.gemm1": (4795508270, 5724960),
+    "decode.gemm2": (2408634871, 7340267),
 }
 
 
@@ -244,29 +244,54 @@ def main():
     quant = {"M": M, "K": K, "ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
              "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
 
-    # dense block-FP8 linear (the layer's E = 1 neighbour), decode and prefill batches
-    from synth import LINEAR_WORKLOAD, make_linear
-    LN, LK = LINEAR_WORKLOAD["N"], LINEAR_WORKLOAD["K"]
-    dense = {"workload": f"DeepSeek-V3-shaped dense down projection N={LN} K={LK}"}
-    for LM in LINEAR_WORKLOAD["M"]:
-        lx, lw, lws = make_linear(LM, LN, LK, 1000 * LINEAR_WORKLOAD["index"], device=dev)
-        lout = torch.empty((LM, LN), dtype=torch.bfloat16, device=dev)
-        lwsp = torch.empty(moe.fp8_block_linear_workspace_bytes(LM, LN, LK), dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            moe.fp8_block_linear(lx, lw, lws, out=lout, workspace=lwsp)
-        le = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        le[0].record()
-        for _ in range(args.steps):
-            moe.fp8_block_linear(lx, lw, lws, out=lout, workspace=lwsp)
-        le[1].record()
-        torch.cuda.synchronize()
-        lms = le[0].elapsed_time(le[1]) / args.steps
-        lbytes = LN * LK + 4 * (LN // 128) * (LK // 128) + 2 * LM * LK + 2 * LM * LN
-        r = roofline_of(lbytes, 2 * LM * LN * LK, lms * 1e-3, MFMA_FP8_PEAK)
-        r.update({"M": LM, "ms": lms, "alg_bytes": lbytes, "alg_flops": 2 * LM * LN * LK})
-        dense[f"M{LM}"] = r
-        del lx, lw, lws, lout, lwsp
+    # the same quantiser with MXFP8 scales: groups of 32, UE8M0 exponent bytes
+    e_out = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(3)]
+    for i in range(3):
+        moe.per_token_group_quant_fp8_fmt(xq_in[i], 32, "ue8m0", q=q_out[i], scales=e_out[i])
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        qe[2 * s].record()
+        moe.per_token_group_quant_fp8_fmt(xq_in[s % 3], 32, "ue8m0", q=q_out[s % 3], scales=e_out[s % 3])
+        qe[2 * s + 1].record()
+    torch.cuda.synchronize()
+    q_ms = float(np.mean([qe[2 * s].elapsed_time(qe[2 * s + 1]) for s in range(args.steps)]))
+    q_bytes = 2 * M * K + M * K + M * (K // 32)
+    quant["mxfp8_group32_ue8m0"] = {"ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
+                                    "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
+    del xq_in, q_out, s_out, e_out
+
+    # dense linears (the layer's E = 1 neighbour), decode and prefill batches:
+    # block FP8 (128x128 weight blocks, float32 scales) and MXFP8 ([1, 32], UE8M0)
+    from synth import LINEAR_WORKLOAD, MX_LINEAR_WORKLOAD, make_linear, make_mx_linear
+
+    def time_linear(fn, ws_bytes, make, wl, scale_bytes):
+        LN, LK = wl["N"], wl["K"]
+        res = {"workload": f"DeepSeek-V3-shaped dense down projection N={LN} K={LK}"}
+        for LM in wl["M"]:
+            lx, lw, lws = make(LM, LN, LK, 1000 * wl["index"], device=dev)
+            lout = torch.empty((LM, LN), dtype=torch.bfloat16, device=dev)
+            lwsp = torch.empty(ws_bytes(LM, LN, LK), dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                fn(lx, lw, lws, out=lout, workspace=lwsp)
+            le = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            le[0].record()
+            for _ in range(args.steps):
+                fn(lx, lw, lws, out=lout, workspace=lwsp)
+            le[1].record()
+            torch.cuda.synchronize()
+            lms = le[0].elapsed_time(le[1]) / args.steps
+            lbytes = LN * LK + scale_bytes(LN, LK) + 2 * LM * LK + 2 * LM * LN
+            r = roofline_of(lbytes, 2 * LM * LN * LK, lms * 1e-3, MFMA_FP8_PEAK)
+            r.update({"M": LM, "ms": lms, "alg_bytes": lbytes, "alg_flops": 2 * LM * LN * LK})
+            res[f"M{LM}"] = r
+            del lx, lw, lws, lout, lwsp
+        return res
+
+    dense = time_linear(moe.fp8_block_linear, moe.fp8_block_linear_workspace_bytes, make_linear,
+                        LINEAR_WORKLOAD, lambda n, k: 4 * (n // 128) * (k // 128))
+    dense_mx = time_linear(moe.mxfp8_linear, moe.mxfp8_linear_workspace_bytes, make_mx_linear,
+                           MX_LINEAR_WORKLOAD, lambda n, k: n * (k // 32))
 
     dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
     dom = kernels[dom_name]
@@ -287,7 +312,8 @@ def main():
         "metric": METRIC, "value": tokens / (wall / args.steps), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8e4m3 (GEMM2 FP8 MFMA, f32 acc; GEMM1 exact f16 MFMA, f64 acc; bf16 in/out)",
+        "dtype": "fp8e4m3 (GEMM2 FP8 MFMA, f32 acc; GEMM1 exact f16 MFMA, f64 acc at decode, "
+                 "f32 at prefill; bf16 in/out)",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}-shaped MoE layer H={H} I={I} E={E} top_k={k}, "
                                + " + ".join(f"{n} T={phases[n]['T']}" for n in order) + " per step",
@@ -297,6 +323,7 @@ def main():
         "phases": result_phases,
         "quant_standalone": quant,
         "dense_linear": dense,
+        "dense_linear_mxfp8": dense_mx,
     }
     if not args.no_cpu_baseline and "decode" in phases:
         ph = phases["decode"]
