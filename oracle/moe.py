@@ -87,15 +87,25 @@ def expert_ffn(x_rows, w13_e, w13s_e, w2_e, w2s_e):
 
 
 def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
-                renormalize: bool, tokens=None):
+                renormalize: bool, tokens=None, num_expert_group=1, topk_group=1,
+                expert_map=None):
     """Whole-layer forward.
 
     x float32 [T, H] (bf16 values), logits float32 [T, E],
-    w13 uint8 [E, 2I, H], w13_scale float32 [E, 2I/128, H/128],
-    w2 uint8 [E, H, I], w2_scale float32 [E, H/128, I/128].
+    w13 uint8 [E_w, 2I, H], w13_scale float32 [E_w, 2I/128, H/128],
+    w2 uint8 [E_w, H, I], w2_scale float32 [E_w, H/128, I/128].
     ``tokens`` optionally restricts the computation to a list of token rows
     (each token's output depends only on its own row, so this gives the same
     values as the full forward at those rows).
+
+    Routing variants: num_expert_group > 1 routes with
+    router.grouped_topk_softmax.  ``expert_map`` (int [E], overview page,
+    "Expert Parallelism and Expert Maps": global -> local expert index, -1
+    for experts held elsewhere) makes the weights those of the E_w local
+    experts: a pair routed to expert e runs local expert expert_map[e], and a
+    pair whose expert maps to -1 contributes zero ("Triton Fused MoE Kernel":
+    zeros are written for such blocks).  The routing weights are those of the
+    global routing either way.
 
     Returns (out float32 [n_tok, H] holding bf16 values, info dict with ids,
     w, xq, xs and per-pair a, aq, as, y in pair order p = row * k + j)."""
@@ -108,11 +118,19 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
     T, H = x.shape
     E = logits.shape[1]
     I = w2.shape[2]
-    ids, w = router.topk_softmax(logits, top_k, renormalize)
+    if num_expert_group > 1:
+        ids, w = router.grouped_topk_softmax(logits, top_k, num_expert_group, topk_group,
+                                             renormalize)
+    else:
+        ids, w = router.topk_softmax(logits, top_k, renormalize)
     xq, xs = quant.per_token_group_quant(x)
 
     P = T * top_k
     flat = ids.reshape(-1)
+    if expert_map is not None:
+        expert_map = np.asarray(expert_map, dtype=np.int64)
+        flat = expert_map[flat]                  # local expert, -1 where absent
+        E = w13.shape[0]
     y = np.zeros((P, H), dtype=np.float64)
     a = np.zeros((P, I), dtype=np.float32)
     aq = np.zeros((P, I), dtype=np.uint8)

@@ -190,3 +190,34 @@ def test_planted_mistakes_fail_brute_force(mutant, monkeypatch):
         monkeypatch.setattr(quant, "per_token_group_quant", inv)
     with pytest.raises(AssertionError):
         test_brute_force_layer(True)
+
+
+# ---- expert map (one rank's share of the experts) ----
+
+def _acc(info, top_k):
+    w = info["w"].astype(np.float64)
+    return sum(w[:, j:j + 1] * info["y"][j::top_k] for j in range(top_k))
+
+
+def test_expert_map_splits_the_layer_into_rank_shares():
+    H, I, E, k, T = 256, 256, 6, 2, 9
+    x, logits = make_activations(H, E, T, seed_base=901)
+    w13, w13s, w2, w2s = make_weights(H, I, E, 902)
+    xf, lf = x.float().numpy(), logits.numpy()
+    ws = [a.numpy() for a in (w13, w13s, w2, w2s)]
+    full, finfo = moe.moe_forward(xf, lf, *ws, k, True)
+    ident, _ = moe.moe_forward(xf, lf, *ws, k, True, expert_map=np.arange(E))
+    assert np.array_equal(ident, full)
+    total = np.zeros((T, H))
+    for local in ([0, 2, 5], [1, 3, 4]):      # two ranks, interleaved placement
+        emap = np.full(E, -1)
+        emap[local] = np.arange(len(local))
+        sub = [a[local] for a in ws]
+        out, info = moe.moe_forward(xf, lf, *sub, k, True, expert_map=emap)
+        assert np.array_equal(info["ids"], finfo["ids"])
+        absent = emap[info["ids"].reshape(-1)] < 0
+        assert np.all(info["y"][absent] == 0)
+        total += _acc(info, k)
+    np.testing.assert_allclose(total, _acc(finfo, k), rtol=1e-12, atol=1e-12)
+    none, _ = moe.moe_forward(xf, lf, *[a[:1] for a in ws], k, True, expert_map=np.full(E, -1))
+    assert np.all(none == 0)

@@ -70,3 +70,64 @@ def test_single_expert():
 def test_bad_k():
     with pytest.raises(ValueError):
         router.topk_softmax(np.zeros((1, 4), np.float32), 5, True)
+
+
+# ---- grouped top-k ----
+
+def _brute_grouped(logits, k, G, kg, renorm):
+    T, E = logits.shape
+    gs = E // G
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float64)
+    for t in range(T):
+        best = []
+        for g in range(G):
+            m = max(float(logits[t, e]) for e in range(g * gs, (g + 1) * gs))
+            best.append((-m, g))
+        kept = {g for _, g in sorted(best)[:kg]}
+        cand = [e for e in range(E) if e // gs in kept]
+        order = sorted(cand, key=lambda e: (-float(logits[t, e]), e))
+        ids[t] = order[:k]
+        p = softmax(logits[t].astype(np.float64))
+        sel = p[order[:k]]
+        w[t] = sel / sel.sum() if renorm else sel
+    return ids, w
+
+
+@pytest.mark.parametrize("T,E,k,G,kg", [(6, 16, 4, 4, 2), (5, 256, 8, 8, 4), (4, 64, 6, 8, 3),
+                                        (3, 32, 2, 32, 2), (4, 12, 3, 3, 1)])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_grouped_brute_force(T, E, k, G, kg, renorm):
+    rng = np.random.default_rng(T * E + k * G + kg)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, :] = np.round(logits[0, :])          # ties inside and across groups
+    ids, w = router.grouped_topk_softmax(logits, k, G, kg, renorm)
+    bids, bw = _brute_grouped(logits, k, G, kg, renorm)
+    assert np.array_equal(ids, bids)
+    np.testing.assert_allclose(w, bw, rtol=1e-7, atol=0)
+
+
+def test_grouped_reduces_to_plain_router():
+    rng = np.random.default_rng(8)
+    logits = rng.standard_normal((20, 64)).astype(np.float32)
+    plain = router.topk_softmax(logits, 8, True)
+    for G, kg in ((1, 1), (8, 8), (64, 64)):
+        g = router.grouped_topk_softmax(logits, 8, G, kg, True)
+        assert np.array_equal(g[0], plain[0]) and np.array_equal(g[1], plain[1])
+
+
+def test_grouped_invariants_and_group_score_is_the_best_logit():
+    rng = np.random.default_rng(9)
+    logits = (rng.standard_normal((100, 128)) * 2).astype(np.float32)
+    ids, w = router.grouped_topk_softmax(logits, 8, 8, 3, True)
+    groups = ids // 16
+    assert all(len(set(r)) <= 3 for r in groups.tolist())
+    gmax = logits.reshape(100, 8, 16).max(axis=2)
+    third = np.sort(gmax, axis=1)[:, ::-1][:, 2]
+    for t in range(100):
+        assert all(gmax[t, g] >= third[t] for g in set(groups[t].tolist()))
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    # one strong expert beats two moderate ones: the score is the maximum, not a sum
+    l = np.array([[5.0, -9, -9, -9, 3.0, 3.0, -9, -9]], np.float32)
+    ids, _ = router.grouped_topk_softmax(l, 2, 2, 1, True)
+    assert ids.tolist() == [[0, 1]]
