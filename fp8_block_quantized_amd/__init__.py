@@ -28,7 +28,8 @@ STAGES = ["router", "align", "quant", "gemm1", "gemm2", "combine"]
 
 EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layout",
            "moe_fp8_forward", "moe_fp8_forward_traced", "per_token_group_quant_fp8",
-           "per_token_group_quant_fp8_fmt", "moe_topk_softmax",
+           "per_token_group_quant_fp8_fmt", "moe_topk_softmax", "moe_topk_softmax_grouped",
+           "moe_fp8_forward_routed",
            "moe_align_scratch_bytes", "moe_align", "moe_status_string",
            "fp8_block_linear_workspace_bytes", "fp8_block_linear",
            "mxfp8_linear_workspace_bytes", "mxfp8_linear"]
@@ -69,6 +70,10 @@ def load_library(path=LIB_PATH):
     lib.per_token_group_quant_fp8_fmt.restype = c_int
     lib.moe_topk_softmax.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp]
     lib.moe_topk_softmax.restype = c_int
+    lib.moe_topk_softmax_grouped.argtypes = [vp] + [c_int] * 6 + [vp, vp, vp]
+    lib.moe_topk_softmax_grouped.restype = c_int
+    lib.moe_fp8_forward_routed.argtypes = [vp] * 6 + [c_int] * 8 + [vp, c_int, vp, vp, c_size, vp]
+    lib.moe_fp8_forward_routed.restype = c_int
     lib.moe_align_scratch_bytes.argtypes = [c_int] * 3
     lib.moe_align_scratch_bytes.restype = c_size
     lib.moe_align.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]
@@ -163,6 +168,31 @@ def moe_fp8_forward(x, router_logits, w13, w13_scale, w2, w2_scale, top_k, renor
     return out
 
 
+def moe_fp8_forward_routed(x, router_logits, w13, w13_scale, w2, w2_scale, top_k, renormalize,
+                           num_expert_group=1, topk_group=1, expert_map=None, out=None,
+                           workspace=None, stream=None):
+    """moe_fp8_forward with grouped top-k and/or an expert map (int32 [E] on the
+    device, global -> local expert or -1); the weights hold the local experts."""
+    T, H = x.shape
+    E = router_logits.shape[1]
+    I = w2.shape[2]
+    EL = w13.shape[0]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, H, I, E, top_k, x.device)
+    emap = None if expert_map is None else _dev(expert_map, torch.int32, "expert_map")
+    st = load_library().moe_fp8_forward_routed(
+        _dev(x, torch.bfloat16, "x"), _dev(router_logits, torch.float32, "router_logits"),
+        _dev(w13, torch.uint8, "w13"), _dev(w13_scale, torch.float32, "w13_scale"),
+        _dev(w2, torch.uint8, "w2"), _dev(w2_scale, torch.float32, "w2_scale"),
+        T, H, I, E, int(top_k), int(bool(renormalize)), int(num_expert_group), int(topk_group),
+        emap, EL, _dev(out, torch.bfloat16, "out"), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check("moe_fp8_forward_routed", st)
+    return out
+
+
 def workspace_taps(workspace, T, H, I, E, top_k):
     """Views of the forward's intermediates inside its workspace."""
     off = moe_fp8_workspace_layout(T, H, I, E, top_k)
@@ -239,6 +269,22 @@ def moe_topk_softmax(logits, top_k, renormalize, ids=None, weights=None, stream=
         _dev(logits, torch.float32, "logits"), T, E, int(top_k), int(bool(renormalize)),
         _dev(ids, torch.int32, "ids"), _dev(weights, torch.float32, "weights"), _stream(stream))
     _check("moe_topk_softmax", st)
+    return ids, weights
+
+
+def moe_topk_softmax_grouped(logits, top_k, num_expert_group, topk_group, renormalize, ids=None,
+                             weights=None, stream=None):
+    """Grouped top-k: logits f32 [T, E] -> (ids int32 [T, k], weights f32 [T, k])."""
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    st = load_library().moe_topk_softmax_grouped(
+        _dev(logits, torch.float32, "logits"), T, E, int(top_k), int(num_expert_group),
+        int(topk_group), int(bool(renormalize)), _dev(ids, torch.int32, "ids"),
+        _dev(weights, torch.float32, "weights"), _stream(stream))
+    _check("moe_topk_softmax_grouped", st)
     return ids, weights
 
 

@@ -24,14 +24,25 @@ namespace moe {
 constexpr int kChunk = 1024;
 constexpr int kMaxE = 512;
 
-__global__ __launch_bounds__(1024) void align_count_kernel(const int32_t* __restrict__ ids, int P,
-                                                           int E, int32_t* __restrict__ counts) {
+// Expert of pair p: ids[p], or through the expert map (global -> local, -1
+// for experts held elsewhere) when one is given.  Anything outside [0, E)
+// leaves the pair out of the layout.
+__device__ __forceinline__ int pair_expert(const int32_t* ids, const int32_t* emap, int n_map, int p) {
+  int e = ids[p];
+  if (emap) e = (unsigned)e < (unsigned)n_map ? emap[e] : -1;
+  return e;
+}
+
+__global__ __launch_bounds__(1024) void align_count_kernel(const int32_t* __restrict__ ids,
+                                                           const int32_t* __restrict__ emap,
+                                                           int n_map, int P, int E,
+                                                           int32_t* __restrict__ counts) {
   __shared__ int hist[kMaxE];
   for (int e = threadIdx.x; e < E; e += kChunk) hist[e] = 0;
   __syncthreads();
   const int p = blockIdx.x * kChunk + threadIdx.x;
   if (p < P) {
-    const int e = ids[p];
+    const int e = pair_expert(ids, emap, n_map, p);
     if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);   // ids outside [0, E) are dropped
   }
   __syncthreads();
@@ -85,14 +96,15 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
 }
 
 __global__ __launch_bounds__(1024) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int ebits, const int32_t* __restrict__ base,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ pair_pos) {
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ emap, int n_map, int P, int E,
+    int ebits, const int32_t* __restrict__ base, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ pair_pos) {
   __shared__ int wcnt[kChunk / 64][kMaxE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < (kChunk / 64) * E; i += kChunk) wcnt[i / E][i % E] = 0;
   __syncthreads();
   const int p = blockIdx.x * kChunk + threadIdx.x;
-  const int e0 = p < P ? ids[p] : -1;
+  const int e0 = p < P ? pair_expert(ids, emap, n_map, p) : -1;
   const bool valid = (unsigned)e0 < (unsigned)E;
   const int e = valid ? e0 : 0;
   unsigned long long peers = __ballot(valid);
@@ -111,6 +123,8 @@ __global__ __launch_bounds__(1024) void align_scatter_kernel(
     const int pos = base[(size_t)blockIdx.x * E + e] + before + rank_in_wave;
     sorted_ids[pos] = p;
     if (pair_pos) pair_pos[p] = pos;
+  } else if (pair_pos && p < P) {
+    pair_pos[p] = -1;            // not in the layout: the combine skips it
   }
 }
 
@@ -153,9 +167,9 @@ const int32_t* align_expert_offsets(const void* scratch, int P, int E) {
   return (const int32_t*)scratch + 2 * nchunk * (size_t)E;
 }
 
-hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
-                        int32_t* expert_ids, int32_t* ntpp, int32_t* pair_pos, void* scratch,
-                        hipStream_t stream) {
+hipError_t launch_align(const int32_t* ids, const int32_t* emap, int n_map, int P, int E, int BM,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, int32_t* pair_pos,
+                        void* scratch, hipStream_t stream) {
   const int nchunk = (P + kChunk - 1) / kChunk;
   int32_t* counts = (int32_t*)scratch;
   int32_t* base = counts + (size_t)nchunk * E;
@@ -163,12 +177,13 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
   int ebits = 0;
   while ((1 << ebits) < E) ++ebits;
   if (nchunk > 0)
-    hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, P, E, counts);
+    hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, emap, n_map,
+                       P, E, counts);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kChunk), 0, stream, counts, nchunk, E, BM, P,
                      base, sorted_ids, expert_ids, ntpp, eoff);
   if (nchunk > 0)
-    hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, P, E, ebits,
-                       base, sorted_ids, pair_pos);
+    hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, emap,
+                       n_map, P, E, ebits, base, sorted_ids, pair_pos);
   return hipGetLastError();
 }
 

@@ -5,7 +5,9 @@
 // the router weight multiplies the dequantised GEMM output):
 //   out[t, :] = bf16( sum over slots j in order of w[t, j] * y[row(t*k + j), :] )
 // accumulated in float32 with one fused multiply-add per term, where row(p)
-// is the sorted row that the second GEMM wrote pair p to.  Each thread
+// is the sorted row that the second GEMM wrote pair p to; a pair left out of
+// the layout (its expert held elsewhere, row -1) contributes zero, the
+// expert map's zero output.  Each thread
 // produces 8 outputs: k gathered 16-byte reads (consecutive threads read
 // consecutive bytes of one row) and one 16-byte write.  HBM bound.
 #include "device_common.hpp"
@@ -23,8 +25,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int jj = 0; jj < top_k; ++jj) {
     const long long p = t * top_k + jj;
+    const int row = pair_pos[p];
+    if (row < 0) continue;
     const float w = topk_w[p];
-    const uint4 v = *(const uint4*)(y + (size_t)pair_pos[p] * ys + c * 8);
+    const uint4 v = *(const uint4*)(y + (size_t)row * ys + c * 8);
     acc[0] = __builtin_fmaf(w, bf16_lo(v.x), acc[0]); acc[1] = __builtin_fmaf(w, bf16_hi(v.x), acc[1]);
     acc[2] = __builtin_fmaf(w, bf16_lo(v.y), acc[2]); acc[3] = __builtin_fmaf(w, bf16_hi(v.y), acc[3]);
     acc[4] = __builtin_fmaf(w, bf16_lo(v.z), acc[4]); acc[5] = __builtin_fmaf(w, bf16_hi(v.z), acc[5]);

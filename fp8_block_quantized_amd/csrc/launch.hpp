@@ -14,13 +14,17 @@ hipError_t launch_group_quant(const void* x, long long M, int K, uint8_t* q, flo
 // group 32 or 128, fmt one of the kScale* values; s is float32 or uint8 per group
 hipError_t launch_group_quant_fmt(const void* x, long long M, int K, int group, int fmt,
                                   uint8_t* q, void* s, hipStream_t stream);
+// num_group > 1: grouped top-k (topk_group of num_group equal expert groups)
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int top_k, int renormalize,
-                               int32_t* ids, float* w, hipStream_t stream);
+                               int num_group, int topk_group, int32_t* ids, float* w,
+                               hipStream_t stream);
 size_t align_scratch_bytes(int P, int E);
 const int32_t* align_expert_offsets(const void* scratch, int P, int E);
-hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
-                        int32_t* expert_ids, int32_t* ntpp, int32_t* pair_pos, void* scratch,
-                        hipStream_t stream);
+// emap (optional, n_map entries): global expert -> local index or -1; pairs whose
+// expert falls outside [0, E) are left out and get pair_pos -1
+hipError_t launch_align(const int32_t* ids, const int32_t* emap, int n_map, int P, int E, int BM,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, int32_t* pair_pos,
+                        void* scratch, hipStream_t stream);
 hipError_t launch_identity_layout(int M, int BM, int nblk, int32_t* sorted_ids,
                                   int32_t* expert_ids, int32_t* eoff, int32_t* ntpp,
                                   hipStream_t stream);

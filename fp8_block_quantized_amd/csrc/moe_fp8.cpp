@@ -170,16 +170,35 @@ int moe_fp8_workspace_layout(int T, int H, int I, int E, int top_k,
   return MOE_OK;
 }
 
+// Routing options of the forward: grouped top-k and an expert map.
+struct Routing {
+  int num_group = 1, topk_group = 1;   // num_group 1: plain top-k
+  const int32_t* emap = nullptr;       // device int32 [E]: global -> local expert or -1
+  int e_local = 0;                     // experts the weights hold (E without a map)
+};
+
+static int check_routing(int E, int top_k, const Routing& r) {
+  if (r.num_group < 1 || r.num_group > 64 || E % r.num_group) return MOE_ERR_SHAPE;
+  if (r.num_group == 1 ? r.topk_group != 1 : (r.topk_group < 1 || r.topk_group > r.num_group))
+    return MOE_ERR_SHAPE;
+  if (top_k > r.topk_group * (E / r.num_group)) return MOE_ERR_SHAPE;
+  if (r.emap ? (r.e_local < 1 || r.e_local > E) : r.e_local != E) return MOE_ERR_SHAPE;
+  if (r.emap && (uintptr_t)r.emap % 4) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 static int forward_impl(const void* x, const float* router_logits, const uint8_t* w13,
                         const float* w13_scale, const uint8_t* w2, const float* w2_scale, int T,
-                        int H, int I, int E, int top_k, int renormalize, void* out,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        int H, int I, int E, int top_k, int renormalize, const Routing& route,
+                        void* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                         hipEvent_t* ev) {
   if (!x || !router_logits || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace)
     return MOE_ERR_NULL;
   int st = check_moe_shape(T, H, I, E, top_k);
   if (st != MOE_OK) return st;
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_SHAPE;
+  if ((st = check_routing(E, top_k, route)) != MOE_OK) return st;
+  const int EL = route.e_local;        // experts of the weights, the layout's experts
   Layout L;
   make_layout(T, H, I, E, top_k, L);
   if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_ERR_WORKSPACE;
@@ -187,15 +206,16 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
       (uintptr_t)router_logits % 4 || (uintptr_t)w13_scale % 4 || (uintptr_t)w2_scale % 4)
     return MOE_ERR_UNSUPPORTED;
   const size_t out_bytes = (size_t)T * H * 2;
-  const size_t w13_bytes = (size_t)E * 2 * I * H, w2_bytes = (size_t)E * H * I;
-  const size_t w13s_bytes = (size_t)E * (2 * I / 128) * (H / 128) * 4;
-  const size_t w2s_bytes = (size_t)E * (H / 128) * (I / 128) * 4;
+  const size_t w13_bytes = (size_t)EL * 2 * I * H, w2_bytes = (size_t)EL * H * I;
+  const size_t w13s_bytes = (size_t)EL * (2 * I / 128) * (H / 128) * 4;
+  const size_t w2s_bytes = (size_t)EL * (H / 128) * (I / 128) * 4;
   if (overlaps(out, out_bytes, x, out_bytes) ||
       overlaps(out, out_bytes, router_logits, (size_t)T * E * 4) ||
       overlaps(out, out_bytes, w13, w13_bytes) || overlaps(out, out_bytes, w2, w2_bytes) ||
       overlaps(out, out_bytes, w13_scale, w13s_bytes) ||
       overlaps(out, out_bytes, w2_scale, w2s_bytes) ||
-      overlaps(out, out_bytes, workspace, L.total))
+      overlaps(out, out_bytes, workspace, L.total) ||
+      (route.emap && overlaps(out, out_bytes, route.emap, (size_t)E * 4)))
     return MOE_ERR_ALIAS;
 
   char* ws = (char*)workspace;
@@ -212,25 +232,29 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
   int32_t* ppos = (int32_t*)(ws + L.off[MOE_TAP_PAIR_POS]);
   void* scratch = ws + L.off[MOE_TAP_ALIGN_SCRATCH];
   const int P = T * top_k;
-  const int nblk = (int)(L.cap / L.BM);
+  // the layout covers the EL local experts: at most P + EL * (BM - 1) rows, within
+  // the workspace sized for E
+  const int nblk = (int)(round_up((size_t)P + (size_t)EL * (L.BM - 1), L.BM) / L.BM);
 
   hipError_t err;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if (mark(0)) return MOE_ERR_HIP;
-  if ((err = moe::launch_topk_softmax(router_logits, T, E, top_k, renormalize, ids, tw, stream)))
+  if ((err = moe::launch_topk_softmax(router_logits, T, E, top_k, renormalize, route.num_group,
+                                      route.topk_group, ids, tw, stream)))
     return MOE_ERR_HIP;
   if (mark(1)) return MOE_ERR_HIP;
-  if ((err = moe::launch_align(ids, P, E, L.BM, sorted, eids, ntpp, ppos, scratch, stream)))
+  if ((err = moe::launch_align(ids, route.emap, E, P, EL, L.BM, sorted, eids, ntpp, ppos, scratch,
+                               stream)))
     return MOE_ERR_HIP;
   if (mark(2)) return MOE_ERR_HIP;
   if ((err = moe::launch_group_quant(x, T, H, xq, xs, stream))) return MOE_ERR_HIP;
   if (mark(3)) return MOE_ERR_HIP;
-  const int32_t* eoff = moe::align_expert_offsets(scratch, P, E);
-  if ((err = moe::launch_gemm1(xq, xs, w13, w13_scale, sorted, eids, ntpp, eoff, E, H, I, P,
+  const int32_t* eoff = moe::align_expert_offsets(scratch, P, EL);
+  if ((err = moe::launch_gemm1(xq, xs, w13, w13_scale, sorted, eids, ntpp, eoff, EL, H, I, P,
                                top_k, L.BM, nblk, aq, as, stream)))
     return MOE_ERR_HIP;
   if (mark(4)) return MOE_ERR_HIP;
-  if ((err = moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, P, L.BM,
+  if ((err = moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, EL, H, I, P, L.BM,
                                nblk, y, (int)y_stride(H), stream)))
     return MOE_ERR_HIP;
   if (mark(5)) return MOE_ERR_HIP;
@@ -244,8 +268,25 @@ int moe_fp8_forward(const void* x, const float* router_logits, const uint8_t* w1
                     const float* w13_scale, const uint8_t* w2, const float* w2_scale, int T,
                     int H, int I, int E, int top_k, int renormalize, void* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Routing r;
+  r.e_local = E;
   return forward_impl(x, router_logits, w13, w13_scale, w2, w2_scale, T, H, I, E, top_k,
-                      renormalize, out, workspace, workspace_bytes, stream, nullptr);
+                      renormalize, r, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_fp8_forward_routed(const void* x, const float* router_logits, const uint8_t* w13,
+                           const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                           int T, int H, int I, int E, int top_k, int renormalize,
+                           int num_expert_group, int topk_group, const int32_t* expert_map,
+                           int num_local_experts, void* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  Routing r;
+  r.num_group = num_expert_group;
+  r.topk_group = topk_group;
+  r.emap = expert_map;
+  r.e_local = num_local_experts;
+  return forward_impl(x, router_logits, w13, w13_scale, w2, w2_scale, T, H, I, E, top_k,
+                      renormalize, r, out, workspace, workspace_bytes, stream, nullptr);
 }
 
 int moe_fp8_forward_traced(const void* x, const float* router_logits, const uint8_t* w13,
@@ -256,8 +297,10 @@ int moe_fp8_forward_traced(const void* x, const float* router_logits, const uint
   if (!events) return MOE_ERR_NULL;
   for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
     if (!events[i]) return MOE_ERR_NULL;
+  Routing r;
+  r.e_local = E;
   return forward_impl(x, router_logits, w13, w13_scale, w2, w2_scale, T, H, I, E, top_k,
-                      renormalize, out, workspace, workspace_bytes, stream, events);
+                      renormalize, r, out, workspace, workspace_bytes, stream, events);
 }
 
 int per_token_group_quant_fp8(const void* x, int M, int K, int group_size, uint8_t* q,
@@ -301,7 +344,28 @@ int moe_topk_softmax(const float* logits, int T, int E, int top_k, int renormali
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
-  return moe::launch_topk_softmax(logits, T, E, top_k, renormalize, topk_ids, topk_weights, stream)
+  return moe::launch_topk_softmax(logits, T, E, top_k, renormalize, 1, 1, topk_ids, topk_weights,
+                                  stream)
+             ? MOE_ERR_HIP
+             : MOE_OK;
+}
+
+int moe_topk_softmax_grouped(const float* logits, int T, int E, int top_k, int num_expert_group,
+                             int topk_group, int renormalize, int32_t* topk_ids,
+                             float* topk_weights, hipStream_t stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || top_k < 1 || top_k > E || top_k > MOE_MAX_TOP_K)
+    return MOE_ERR_SHAPE;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_SHAPE;
+  Routing r;
+  r.num_group = num_expert_group;
+  r.topk_group = topk_group;
+  r.e_local = E;
+  const int st = check_routing(E, top_k, r);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  return moe::launch_topk_softmax(logits, T, E, top_k, renormalize, num_expert_group, topk_group,
+                                  topk_ids, topk_weights, stream)
              ? MOE_ERR_HIP
              : MOE_OK;
 }
@@ -324,8 +388,8 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m, int
   const int P = T * top_k;
   if (scratch_bytes < moe::align_scratch_bytes(P, E) || ((uintptr_t)scratch % 4))
     return MOE_ERR_WORKSPACE;
-  return moe::launch_align(topk_ids, P, E, block_m, sorted_ids, expert_ids, num_tokens_post_padded,
-                           nullptr, scratch, stream)
+  return moe::launch_align(topk_ids, nullptr, 0, P, E, block_m, sorted_ids, expert_ids,
+                           num_tokens_post_padded, nullptr, scratch, stream)
              ? MOE_ERR_HIP
              : MOE_OK;
 }

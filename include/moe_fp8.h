@@ -128,6 +128,43 @@ int moe_fp8_forward(const void* x, const float* router_logits,
                     void* out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/*
+ * moe_fp8_forward with the routing variants of the pages:
+ *   - grouped top-k (num_expert_group > 1; the overview page's environment
+ *     table names a fused grouped top-K routing switch without defining it,
+ *     read here in the router's own terms): the E experts form
+ *     num_expert_group equal groups of consecutive ids, a group's score is its
+ *     best logit, the topk_group best groups are kept (ties to the lower
+ *     group), and the top_k experts are chosen among the kept groups' experts
+ *     as moe_topk_softmax chooses them; the weights are the same full softmax,
+ *     renormalised over the chosen slots if asked.  num_expert_group == 1
+ *     (with topk_group == 1) is the plain router.
+ *   - an expert map (overview page, "Expert Parallelism and Expert Maps":
+ *     global expert -> local index, -1 for experts on other ranks; "Triton
+ *     Fused MoE Kernel": zeros are written for blocks of absent experts):
+ *     expert_map is device int32 [E]; w13, w2 and their scales hold the
+ *     num_local_experts local experts; a pair routed to an expert mapped
+ *     outside [0, num_local_experts) contributes zero to out, so out is this
+ *     rank's share of the layer, the sum over ranks being the full layer.
+ *     Routing (ids and weights, MOE_TAP_TOPK_*) is over the E global logits;
+ *     MOE_TAP_EXPERT_IDS and the sorted layout are over local experts, and
+ *     MOE_TAP_PAIR_POS is -1 for the pairs left out.  expert_map NULL requires
+ *     num_local_experts == E.
+ * Constraints: those of moe_fp8_forward, plus 1 <= num_expert_group <= 64
+ * dividing E, 1 <= topk_group <= num_expert_group, top_k <= topk_group * E /
+ * num_expert_group, 1 <= num_local_experts <= E, expert_map 4-byte aligned and
+ * not overlapping out.  The workspace is moe_fp8_workspace_bytes(T, H, I, E,
+ * top_k) with the global E (it bounds the local layout).
+ */
+int moe_fp8_forward_routed(const void* x, const float* router_logits,
+                           const uint8_t* w13, const float* w13_scale,
+                           const uint8_t* w2, const float* w2_scale,
+                           int T, int H, int I, int E, int top_k, int renormalize,
+                           int num_expert_group, int topk_group,
+                           const int32_t* expert_map, int num_local_experts,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* Stages of the forward, in launch order (for moe_fp8_forward_traced). */
 enum {
   MOE_STAGE_ROUTER = 0,     /* softmax top-k */
@@ -210,6 +247,12 @@ int per_token_group_quant_fp8_fmt(const void* x, int M, int K, int group_size, i
  */
 int moe_topk_softmax(const float* logits, int T, int E, int top_k, int renormalize,
                      int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/* Router stage alone with grouped top-k (the routing of moe_fp8_forward_routed;
+ * same kernel).  Constraints as there. */
+int moe_topk_softmax_grouped(const float* logits, int T, int E, int top_k, int num_expert_group,
+                             int topk_group, int renormalize, int32_t* topk_ids,
+                             float* topk_weights, hipStream_t stream);
 
 /* Bytes of int32 scratch moe_align needs for P = T*top_k pairs and E experts. */
 size_t moe_align_scratch_bytes(int T, int top_k, int E);

@@ -201,3 +201,32 @@ def test_mx_linear_workspace_and_argument_checks():
     assert f(*bad) == -3                         # exponent bytes not 4-byte aligned
     bad = list(ok); bad[6] = vp(0x30000 + 16)
     assert f(*bad) == -6                         # out overlaps the exponents (N*K/32 bytes)
+
+
+def test_routing_argument_checks():
+    # every call below is invalid, so it returns before anything is launched
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    g = lib.moe_topk_softmax_grouped
+    assert g(vp(16), 4, 256, 8, 7, 4, 1, vp(64), vp(128), None) == -2     # 7 does not divide 256
+    assert g(vp(16), 4, 256, 8, 8, 9, 1, vp(64), vp(128), None) == -2     # topk_group > groups
+    assert g(vp(16), 4, 256, 8, 128, 1, 1, vp(64), vp(128), None) == -2   # more than 64 groups
+    assert g(vp(16), 4, 256, 8, 64, 1, 1, vp(64), vp(128), None) == -2    # top_k > kept experts (4)
+    assert g(vp(16), 4, 256, 8, 1, 2, 1, vp(64), vp(128), None) == -2     # one group needs topk_group 1
+    assert g(None, 4, 256, 8, 8, 4, 1, vp(64), vp(128), None) == -1
+    assert g(None, 0, 256, 8, 8, 4, 1, None, None, None) == 0             # empty: no-op
+    T, H, I, E, k = 4, 256, 256, 16, 2
+    n = lib.moe_fp8_workspace_bytes(T, H, I, E, k)
+    f = lib.moe_fp8_forward_routed
+    base = [vp(0x10000 * (i + 1)) for i in range(6)] + [T, H, I, E, k, 1, 1, 1, vp(0x900000), 8,
+                                                         vp(0x100000), vp(0x7000000000), n, None]
+
+    def call(a):
+        return f(*a)
+    a = list(base); a[15] = 17; assert call(a) == -2        # more local experts than E
+    a = list(base); a[15] = 0; assert call(a) == -2
+    a = list(base); a[14] = None; assert call(a) == -2      # no map: local count must be E
+    a = list(base); a[14] = vp(0x900002); assert call(a) == -3     # map misaligned
+    a = list(base); a[14] = vp(0x100000 + 8); assert call(a) == -6   # map inside out
+    a = list(base); a[12], a[13] = 4, 5; assert call(a) == -2      # topk_group > num_expert_group
+    a = list(base); a[12], a[13] = 8, 1; a[10] = 3; assert call(a) == -2   # top_k 3 > one group of 2
