@@ -152,3 +152,33 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
     info = {"ids": ids, "w": w, "xq": xq, "xs": xs, "a": a, "aq": aq,
             "as": as_, "y": y}
     return out, info
+
+
+def batched_experts(x, counts, w13, w13_scale, w2, w2_scale):
+    """The expert computation in the batched activation format.
+
+    Source: overview page, "FusedMoEPermuteExpertsUnpermute Implementations"
+    (BatchedDeepGemmExperts: the masked grouped GEMM of the FP8 block scheme)
+    and the fp8 oracle API page's BatchedExperts activation format; the pages
+    define nothing further, so the reading is the plainest one: activations
+    already dispatched per expert, x [E, M, H], of which expert e's first
+    counts[e] rows are real; each real row goes through that expert's steps
+    2-7 (quantise, GEMM1, SiLU*mul, requantise, GEMM2); the routing weights
+    belong to the finalize step, not to the experts.
+
+    Returns (out float32 [E, M, H] holding bf16 values, zero at rows
+    r >= counts[e], info with the float64 y per expert)."""
+    x = np.asarray(x, dtype=np.float32)
+    E, M, H = x.shape
+    counts = np.asarray(counts, dtype=np.int64)
+    out = np.zeros((E, M, H), dtype=np.float32)
+    ys = []
+    for e in range(E):
+        c = int(counts[e])
+        if c <= 0:
+            ys.append(np.zeros((0, H)))
+            continue
+        r = expert_ffn(x[e, :c], w13[e], w13_scale[e], w2[e], w2_scale[e])
+        out[e, :c] = bf16_round(r["y"])
+        ys.append(r["y"])
+    return out, {"y": ys}

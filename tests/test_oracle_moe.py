@@ -221,3 +221,54 @@ def test_expert_map_splits_the_layer_into_rank_shares():
     np.testing.assert_allclose(total, _acc(finfo, k), rtol=1e-12, atol=1e-12)
     none, _ = moe.moe_forward(xf, lf, *[a[:1] for a in ws], k, True, expert_map=np.full(E, -1))
     assert np.all(none == 0)
+
+
+# ---- batched activation format ----
+
+def test_batched_experts_dispatch_then_combine_equals_the_layer():
+    """Dispatch a routed layer into the batched format (expert e's rows are
+    its pairs' tokens in ascending pair order), run the batched experts, and
+    combine with the routing weights: the float64 sum equals the standard
+    forward's before rounding, and the rows past each count are zero."""
+    H, I, E, k, T = 256, 256, 5, 2, 13
+    x, logits = make_activations(H, E, T, seed_base=911)
+    w13, w13s, w2, w2s = make_weights(H, I, E, 912)
+    xf, lf = x.float().numpy(), logits.numpy()
+    ws = [a.numpy() for a in (w13, w13s, w2, w2s)]
+    full, finfo = moe.moe_forward(xf, lf, *ws, k, True)
+    flat = finfo["ids"].reshape(-1)
+    M = 9
+    xb = np.full((E, M, H), np.nan, np.float32)          # rows past the counts are never read
+    counts = np.zeros(E, np.int64)
+    slot = {}
+    for p in range(T * k):
+        e = int(flat[p])
+        slot[p] = (e, counts[e])
+        xb[e, counts[e]] = xf[p // k]
+        counts[e] += 1
+    assert counts.max() <= M
+    out, binfo = moe.batched_experts(xb, counts, *ws)
+    acc = np.zeros((T, H))
+    for p, (e, r) in slot.items():
+        acc[p // k] += float(finfo["w"].reshape(-1)[p]) * binfo["y"][e][r]
+    np.testing.assert_allclose(acc, _acc(finfo, k), rtol=1e-12, atol=1e-12)
+    for e in range(E):
+        assert np.all(out[e, counts[e]:] == 0)
+        assert np.array_equal(out[e, :counts[e]], moe.bf16_round(binfo["y"][e]))
+
+
+def test_batched_experts_rows_are_independent():
+    H, I, E, M = 256, 128, 3, 6
+    g = torch.Generator().manual_seed(5)
+    xb = torch.randn((E, M, H), generator=g).to(torch.bfloat16).float().numpy()
+    w13, w13s, w2, w2s = make_weights(H, I, E, 913)
+    ws = [a.numpy() for a in (w13, w13s, w2, w2s)]
+    counts = np.array([6, 0, 4])
+    out, _ = moe.batched_experts(xb, counts, *ws)
+    assert np.all(out[1] == 0)
+    perm = np.array([3, 1, 0, 2])
+    xp = xb.copy()
+    xp[2, :4] = xb[2, perm]
+    outp, _ = moe.batched_experts(xp, counts, *ws)
+    assert np.array_equal(outp[2, :4], out[2, perm])
+    assert np.array_equal(outp[0], out[0])
