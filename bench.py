@@ -293,6 +293,41 @@ def main():
     dense_mx = time_linear(moe.mxfp8_linear, moe.mxfp8_linear_workspace_bytes, make_mx_linear,
                            MX_LINEAR_WORKLOAD, lambda n, k: n * (k // 32))
 
+    # batched (masked) expert format: one rank's experts, device-side counts
+    from synth import BATCHED_WORKLOAD as BW
+    bE, bM, bH, bI = BW["E"], BW["M"], BW["H"], BW["I"]
+    gb = torch.Generator(device="cpu").manual_seed(1000 * BW["index"] + 1)
+    bcounts = torch.randint(BW["min_count"], bM + 1, (bE,), generator=gb, dtype=torch.int32)
+    bx = torch.randn((bE, bM, bH), generator=torch.Generator(device=dev).manual_seed(1000 * BW["index"]),
+                     device=dev).to(torch.bfloat16)
+    bw = make_weights(bH, bI, bE, 1000 * BW["index"] + 2, dev)
+    bc_dev = bcounts.to(dev)
+    bout = torch.empty_like(bx)
+    bws = torch.empty(moe.moe_fp8_batched_workspace_bytes(bE, bM, bH, bI), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws)
+    be = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    be[0].record()
+    for _ in range(args.steps):
+        moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws)
+    be[1].record()
+    torch.cuda.synchronize()
+    bms = be[0].elapsed_time(be[1]) / args.steps
+    rows = int(bcounts.sum())
+    active = int((bcounts > 0).sum())
+    wbytes = active * (2 * bI * bH + bH * bI + 4 * (2 * bI // 128) * (bH // 128) + 4 * (bH // 128) * (bI // 128))
+    bbytes = wbytes + 2 * rows * bH + 2 * bE * bM * bH
+    bflops = 6 * rows * bH * bI
+    # GEMM1 (4 H I flops per row) runs on f16 MFMAs, GEMM2 (2 H I) on FP8 ones:
+    # the peak of the mix is 6 / (4 / f16 peak + 2 / FP8 peak)
+    blend = 6.0 / (4.0 / MFMA_F16_PEAK + 2.0 / MFMA_FP8_PEAK)
+    batched = roofline_of(bbytes, bflops, bms * 1e-3, blend)
+    batched.update({"workload": f"DeepSeek-V3-shaped experts of one rank of eight: E={bE} max_tokens={bM} "
+                                f"H={bH} I={bI}, counts uniform in [{BW['min_count']}, {bM}]",
+                    "rows": rows, "ms": bms, "alg_bytes": bbytes, "alg_flops": bflops})
+    del bx, bw, bout, bws
+
     dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
     dom = kernels[dom_name]
     roof = roofline_of(dom["bytes"], dom["flops"], dom["ms"] * 1e-3, dom["peak"])
@@ -324,6 +359,7 @@ def main():
         "quant_standalone": quant,
         "dense_linear": dense,
         "dense_linear_mxfp8": dense_mx,
+        "batched_experts": batched,
     }
     if not args.no_cpu_baseline and "decode" in phases:
         ph = phases["decode"]

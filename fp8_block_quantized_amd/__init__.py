@@ -29,7 +29,7 @@ STAGES = ["router", "align", "quant", "gemm1", "gemm2", "combine"]
 EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layout",
            "moe_fp8_forward", "moe_fp8_forward_traced", "per_token_group_quant_fp8",
            "per_token_group_quant_fp8_fmt", "moe_topk_softmax", "moe_topk_softmax_grouped",
-           "moe_fp8_forward_routed",
+           "moe_fp8_forward_routed", "moe_fp8_batched_workspace_bytes", "moe_fp8_batched_experts",
            "moe_align_scratch_bytes", "moe_align", "moe_status_string",
            "fp8_block_linear_workspace_bytes", "fp8_block_linear",
            "mxfp8_linear_workspace_bytes", "mxfp8_linear"]
@@ -74,6 +74,10 @@ def load_library(path=LIB_PATH):
     lib.moe_topk_softmax_grouped.restype = c_int
     lib.moe_fp8_forward_routed.argtypes = [vp] * 6 + [c_int] * 8 + [vp, c_int, vp, vp, c_size, vp]
     lib.moe_fp8_forward_routed.restype = c_int
+    lib.moe_fp8_batched_workspace_bytes.argtypes = [c_int] * 4
+    lib.moe_fp8_batched_workspace_bytes.restype = c_size
+    lib.moe_fp8_batched_experts.argtypes = [vp] * 6 + [c_int] * 4 + [vp, vp, c_size, vp]
+    lib.moe_fp8_batched_experts.restype = c_int
     lib.moe_align_scratch_bytes.argtypes = [c_int] * 3
     lib.moe_align_scratch_bytes.restype = c_size
     lib.moe_align.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]
@@ -355,4 +359,31 @@ def mxfp8_linear(x, w, w_scale, out=None, workspace=None, stream=None):
         M, N, K, _dev(out, torch.bfloat16, "out"), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream))
     _check("mxfp8_linear", st)
+    return out
+
+
+def moe_fp8_batched_workspace_bytes(E, max_tokens, H, I):
+    return load_library().moe_fp8_batched_workspace_bytes(E, max_tokens, H, I)
+
+
+def moe_fp8_batched_experts(x, expert_num_tokens, w13, w13_scale, w2, w2_scale, out=None,
+                            workspace=None, stream=None):
+    """Batched (masked) expert format: x bf16 [E, M, H], expert_num_tokens int32
+    [E] on the device -> out bf16 [E, M, H] (zero past each count)."""
+    E, M, H = x.shape
+    I = w2.shape[2]
+    if out is None:
+        out = torch.empty((E, M, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        n = moe_fp8_batched_workspace_bytes(E, M, H, I)
+        if n == 0:
+            raise MoeError("moe_fp8_batched_workspace_bytes", -2)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    st = load_library().moe_fp8_batched_experts(
+        _dev(x, torch.bfloat16, "x"), _dev(expert_num_tokens, torch.int32, "expert_num_tokens"),
+        _dev(w13, torch.uint8, "w13"), _dev(w13_scale, torch.float32, "w13_scale"),
+        _dev(w2, torch.uint8, "w2"), _dev(w2_scale, torch.float32, "w2_scale"),
+        E, M, H, I, _dev(out, torch.bfloat16, "out"), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check("moe_fp8_batched_experts", st)
     return out

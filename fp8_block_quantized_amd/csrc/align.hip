@@ -155,6 +155,73 @@ hipError_t launch_identity_layout(int M, int BM, int nblk, int32_t* sorted_ids,
   return hipGetLastError();
 }
 
+// The layout of the batched activation format: token t = e * M + r is row r
+// of expert e, and expert e's first counts[e] rows (clamped to [0, M]) are
+// real.  One workgroup: the padded expert offsets are a scan over E, then
+// the sorted rows (t for real rows, the sentinel E * M for padding), the
+// block -> expert table and the token -> row map (-1 for rows past a count,
+// which the combine writes as zeros) are filled by all threads.
+__global__ __launch_bounds__(1024) void batched_layout_kernel(
+    const int32_t* __restrict__ counts, int E, int M, int BM, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp, int32_t* __restrict__ eoff,
+    int32_t* __restrict__ pair_pos) {
+  __shared__ int scan[kChunk];
+  __shared__ int cnt[kMaxE], off[kMaxE];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) {
+    c = counts[e];
+    c = c < 0 ? 0 : (c > M ? M : c);
+    cnt[e] = c;
+  }
+  const int pad = (c + BM - 1) / BM * BM;
+  scan[e] = pad;
+  __syncthreads();
+  for (int o = 1; o < kChunk; o <<= 1) {
+    const int v = e >= o ? scan[e - o] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int total = scan[kChunk - 1];
+  if (e < E) {
+    off[e] = scan[e] - pad;
+    eoff[e] = (scan[e] - pad) / BM;
+  }
+  if (e == 0) {
+    eoff[E] = total / BM;
+    ntpp[0] = total;
+  }
+  __syncthreads();
+  const int P = E * M;
+  for (int blk = threadIdx.x; blk < total / BM; blk += kChunk) {
+    int lo = 0, hi = E - 1;  // first expert with inclusive end > row
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (scan[mid] > blk * BM) hi = mid; else lo = mid + 1;
+    }
+    expert_ids[blk] = lo;
+  }
+  for (int t = threadIdx.x; t < P; t += kChunk) {
+    const int te = t / M, r = t - te * M;
+    const bool real = r < cnt[te];
+    if (real) sorted_ids[off[te] + r] = t;
+    pair_pos[t] = real ? off[te] + r : -1;
+  }
+  for (int i = threadIdx.x; i < E * BM; i += kChunk) {   // padding after each expert's rows
+    const int pe = i / BM, r = cnt[pe] + (i - pe * BM);
+    if (r < (cnt[pe] + BM - 1) / BM * BM) sorted_ids[off[pe] + r] = P;
+  }
+}
+
+hipError_t launch_batched_layout(const int32_t* counts, int E, int M, int BM, int32_t* sorted_ids,
+                                 int32_t* expert_ids, int32_t* ntpp, int32_t* eoff,
+                                 int32_t* pair_pos, hipStream_t stream) {
+  hipLaunchKernelGGL(batched_layout_kernel, dim3(1), dim3(kChunk), 0, stream, counts, E, M, BM,
+                     sorted_ids, expert_ids, ntpp, eoff, pair_pos);
+  return hipGetLastError();
+}
+
 // scratch: per-chunk counts and bases [nchunk, E] each, then the expert
 // block offsets [E + 1] that the GEMMs use to order their tiles
 size_t align_scratch_bytes(int P, int E) {

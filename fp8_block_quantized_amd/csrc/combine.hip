@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     const long long p = t * top_k + jj;
     const int row = pair_pos[p];
     if (row < 0) continue;
-    const float w = topk_w[p];
+    const float w = topk_w ? topk_w[p] : 1.0f;     // no weights: copy (1 * y is exact)
     const uint4 v = *(const uint4*)(y + (size_t)row * ys + c * 8);
     acc[0] = __builtin_fmaf(w, bf16_lo(v.x), acc[0]); acc[1] = __builtin_fmaf(w, bf16_hi(v.x), acc[1]);
     acc[2] = __builtin_fmaf(w, bf16_lo(v.y), acc[2]); acc[3] = __builtin_fmaf(w, bf16_hi(v.y), acc[3]);

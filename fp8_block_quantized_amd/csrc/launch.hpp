@@ -47,6 +47,14 @@ hipError_t launch_gemm2_bounded(const uint8_t* act, const float* act_scale, cons
                                 int N, int K, int P, int BM, int nblk, uint16_t* y, int y_stride,
                                 int y_rows, int y_cols, uint16_t* y_dump, int ksplit, float* part,
                                 bool mx, hipStream_t stream);
+// quantise rows [e*M, e*M + counts[e]) of x [E*M, K] (group 128, float32 scales)
+hipError_t launch_group_quant_masked(const void* x, const int32_t* counts, int E, int M, int K,
+                                     uint8_t* q, float* s, hipStream_t stream);
+// sorted layout of the batched format (token e*M + r = row r of expert e, counts[e] real rows)
+hipError_t launch_batched_layout(const int32_t* counts, int E, int M, int BM, int32_t* sorted_ids,
+                                 int32_t* expert_ids, int32_t* ntpp, int32_t* eoff,
+                                 int32_t* pair_pos, hipStream_t stream);
+// topk_w NULL: unit weights (a gather of the rows, zeros for row -1)
 hipError_t launch_combine(const uint16_t* y, int y_stride, const int32_t* pair_pos,
                           const float* topk_w, int T, int H, int top_k, uint16_t* out,
                           hipStream_t stream);

@@ -303,6 +303,67 @@ int moe_fp8_forward_traced(const void* x, const float* router_logits, const uint
                       renormalize, r, out, workspace, workspace_bytes, stream, events);
 }
 
+// The batched expert format uses the forward's layout for T = E * max_tokens
+// tokens routed to one slot each (token e * max_tokens + r is row r of expert e).
+size_t moe_fp8_batched_workspace_bytes(int E, int max_tokens, int H, int I) {
+  if (E < 1 || max_tokens < 1 || (long long)E * max_tokens > MOE_MAX_TOKENS) return 0;
+  return moe_fp8_workspace_bytes(E * max_tokens, H, I, E, 1);
+}
+
+int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, const uint8_t* w13,
+                            const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                            int E, int max_tokens, int H, int I, void* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (E < 1 || max_tokens < 1 || (long long)E * max_tokens > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
+  const int T = E * max_tokens;
+  int st = check_moe_shape(T, H, I, E, 1);
+  if (st != MOE_OK) return st;
+  if (!x || !expert_num_tokens || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace)
+    return MOE_ERR_NULL;
+  Layout L;
+  make_layout(T, H, I, E, 1, L);
+  if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)x % 16 || (uintptr_t)out % 16 || (uintptr_t)w13 % 16 || (uintptr_t)w2 % 16 ||
+      (uintptr_t)expert_num_tokens % 4 || (uintptr_t)w13_scale % 4 || (uintptr_t)w2_scale % 4)
+    return MOE_ERR_UNSUPPORTED;
+  const size_t out_bytes = (size_t)T * H * 2;
+  const size_t w13_bytes = (size_t)E * 2 * I * H, w2_bytes = (size_t)E * H * I;
+  const size_t w13s_bytes = (size_t)E * (2 * I / 128) * (H / 128) * 4;
+  const size_t w2s_bytes = (size_t)E * (H / 128) * (I / 128) * 4;
+  if (overlaps(out, out_bytes, x, out_bytes) || overlaps(out, out_bytes, w13, w13_bytes) ||
+      overlaps(out, out_bytes, w2, w2_bytes) || overlaps(out, out_bytes, w13_scale, w13s_bytes) ||
+      overlaps(out, out_bytes, w2_scale, w2s_bytes) ||
+      overlaps(out, out_bytes, expert_num_tokens, (size_t)E * 4) ||
+      overlaps(out, out_bytes, workspace, L.total))
+    return MOE_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  int32_t* sorted = (int32_t*)(ws + L.off[MOE_TAP_SORTED_IDS]);
+  int32_t* eids = (int32_t*)(ws + L.off[MOE_TAP_EXPERT_IDS]);
+  int32_t* ntpp = (int32_t*)(ws + L.off[MOE_TAP_NTPP]);
+  int32_t* ppos = (int32_t*)(ws + L.off[MOE_TAP_PAIR_POS]);
+  uint8_t* xq = (uint8_t*)(ws + L.off[MOE_TAP_XQ]);
+  float* xs = (float*)(ws + L.off[MOE_TAP_XS]);
+  uint8_t* aq = (uint8_t*)(ws + L.off[MOE_TAP_AQ]);
+  float* as = (float*)(ws + L.off[MOE_TAP_AS]);
+  uint16_t* y = (uint16_t*)(ws + L.off[MOE_TAP_Y]);
+  int32_t* eoff = (int32_t*)(ws + L.off[MOE_TAP_ALIGN_SCRATCH]);   // [E + 1]
+  const int nblk = (int)(L.cap / L.BM);
+  if (moe::launch_batched_layout(expert_num_tokens, E, max_tokens, L.BM, sorted, eids, ntpp, eoff,
+                                 ppos, stream))
+    return MOE_ERR_HIP;
+  if (moe::launch_group_quant_masked(x, expert_num_tokens, E, max_tokens, H, xq, xs, stream))
+    return MOE_ERR_HIP;
+  if (moe::launch_gemm1(xq, xs, w13, w13_scale, sorted, eids, ntpp, eoff, E, H, I, T, 1, L.BM,
+                        nblk, aq, as, stream))
+    return MOE_ERR_HIP;
+  if (moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, T, L.BM, nblk, y,
+                        (int)y_stride(H), stream))
+    return MOE_ERR_HIP;
+  if (moe::launch_combine(y, (int)y_stride(H), ppos, nullptr, T, H, 1, (uint16_t*)out, stream))
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 int per_token_group_quant_fp8(const void* x, int M, int K, int group_size, uint8_t* q,
                               float* scales, hipStream_t stream) {
   if (group_size != MOE_QUANT_GROUP) return MOE_ERR_UNSUPPORTED;

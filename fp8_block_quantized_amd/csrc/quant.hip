@@ -31,11 +31,24 @@ __device__ __forceinline__ uint32_t ceil_pow2_bits(float s) {
   return (b & 0x7FFFFFu) ? (b & 0x7F800000u) + 0x00800000u : b;
 }
 
-template <int G, int FMT, int SLOTS>
+// kMasked: the rows form E blocks of M rows (blockIdx.y = block e) of which
+// only the first counts[e] are quantised (the batched expert format); the
+// others are neither read nor written.
+template <int G, int FMT, int SLOTS, bool kMasked = false>
 __global__ __launch_bounds__(256) void group_quant_bf16_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, void* __restrict__ scales,
-    long long nslots) {
+    long long nslots, const int32_t* __restrict__ counts = nullptr, int M = 0,
+    int slots_per_row = 0) {
   constexpr int LPG = G / 8;   // lanes per group
+  if (kMasked) {   // this block's expert: its rows start at e * M
+    int c = counts[blockIdx.y];
+    c = c < 0 ? 0 : (c > M ? M : c);
+    const long long first = (long long)blockIdx.y * M * slots_per_row;
+    x += first;
+    q += first;
+    scales = (uint8_t*)scales + first / LPG * (FMT == kScaleUe8m0 ? 1 : 4);
+    nslots = (long long)c * slots_per_row;
+  }
   const long long base = ((long long)blockIdx.x * 256 * SLOTS) + threadIdx.x;
   uint4 v[SLOTS];
 #pragma unroll
@@ -113,6 +126,18 @@ hipError_t launch_group_quant_fmt(const void* x, long long M, int K, int group, 
 hipError_t launch_group_quant(const void* x, long long M, int K, uint8_t* q, float* s,
                               hipStream_t stream) {
   return launch_group_quant_fmt(x, M, K, 128, kScaleFloat32, q, s, stream);
+}
+
+hipError_t launch_group_quant_masked(const void* x, const int32_t* counts, int E, int M, int K,
+                                     uint8_t* q, float* s, hipStream_t stream) {
+  constexpr int SLOTS = 2;
+  const long long per = (long long)M * (K / 8);
+  if (per == 0 || E == 0) return hipSuccess;
+  const unsigned nbx = (unsigned)((per + 256LL * SLOTS - 1) / (256LL * SLOTS));
+  hipLaunchKernelGGL((group_quant_bf16_kernel<128, kScaleFloat32, SLOTS, true>), dim3(nbx, E),
+                     dim3(256), 0, stream, (const uint4*)x, (uint2*)q, (void*)s, per, counts, M,
+                     K / 8);
+  return hipGetLastError();
 }
 
 }  // namespace moe

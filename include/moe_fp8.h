@@ -165,6 +165,41 @@ int moe_fp8_forward_routed(const void* x, const float* router_logits,
                            void* out, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * The expert computation in the batched activation format (overview page,
+ * "FusedMoEPermuteExpertsUnpermute Implementations": BatchedDeepGemmExperts,
+ * the masked grouped GEMM of the FP8 block scheme; fp8 oracle API page, the
+ * BatchedExperts activation format): the tokens are already dispatched per
+ * expert, and expert e's rows [0, expert_num_tokens[e]) of x[e] are real.
+ *   for every e and r < expert_num_tokens[e] (clamped to [0, max_tokens]):
+ *     out[e, r] = bf16( the layer's expert steps on x[e, r] with expert e:
+ *                       128-group quant, GEMM1, SiLU*mul, requant, GEMM2 )
+ *   out[e, r] = 0 for the rows past the count.
+ * No routing weight is applied: in this format it belongs to the finalize
+ * step.  The counts stay on the device (the host never reads them), so a
+ * caller can replay the call with new counts; an expert with no row costs
+ * no GEMM work.
+ *
+ *   x                 bf16    [E, max_tokens, H]  (rows past the counts are never read)
+ *   expert_num_tokens int32   [E]                 device
+ *   w13, w13_scale, w2, w2_scale as in moe_fp8_forward (E experts)
+ *   out               bf16    [E, max_tokens, H]; must not overlap any input
+ *   workspace         moe_fp8_batched_workspace_bytes(E, max_tokens, H, I) bytes,
+ *                     256-byte aligned; its MOE_TAP_* tensors are those of
+ *                     moe_fp8_workspace_layout(E * max_tokens, H, I, E, 1) with
+ *                     token e * max_tokens + r (the router taps are unused, and
+ *                     MOE_TAP_ALIGN_SCRATCH holds the expert block offsets)
+ * Constraints: E * max_tokens <= MOE_MAX_TOKENS, E <= MOE_MAX_EXPERTS, H and I
+ * multiples of 128 as in moe_fp8_forward.
+ */
+size_t moe_fp8_batched_workspace_bytes(int E, int max_tokens, int H, int I);
+int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens,
+                            const uint8_t* w13, const float* w13_scale,
+                            const uint8_t* w2, const float* w2_scale,
+                            int E, int max_tokens, int H, int I,
+                            void* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* Stages of the forward, in launch order (for moe_fp8_forward_traced). */
 enum {
   MOE_STAGE_ROUTER = 0,     /* softmax top-k */

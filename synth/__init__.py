@@ -42,6 +42,10 @@ LINEAR_WORKLOAD = dict(index=5, N=7168, K=18432, M=(64, 8192))
 # The same dense shape with MXFP8 operands: [1, 32] blocks, UE8M0 scales
 MX_LINEAR_WORKLOAD = dict(index=6, N=7168, K=18432, M=(64, 8192))
 MX_BLOCK = 32
+# Batched (masked) expert format: the 32 experts of one rank of an 8-way
+# DeepSeek-V3 expert placement, up to 256 dispatched rows each, seeded counts
+# uniform in [64, 256]
+BATCHED_WORKLOAD = dict(index=7, E=32, M=256, H=7168, I=2048, min_count=64)
 
 WEIGHT_STD = 0.02
 BLOCK = 128

@@ -230,3 +230,21 @@ def test_routing_argument_checks():
     a = list(base); a[14] = vp(0x100000 + 8); assert call(a) == -6   # map inside out
     a = list(base); a[12], a[13] = 4, 5; assert call(a) == -2      # topk_group > num_expert_group
     a = list(base); a[12], a[13] = 8, 1; a[10] = 3; assert call(a) == -2   # top_k 3 > one group of 2
+
+
+def test_batched_argument_checks():
+    # every call below is invalid, so it returns before anything is launched
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    assert moe.moe_fp8_batched_workspace_bytes(4, 16, 256, 256) == moe.moe_fp8_workspace_bytes(64, 256, 256, 4, 1)
+    assert moe.moe_fp8_batched_workspace_bytes(64, 512, 256, 256) == 0          # E * M > 16384
+    n = moe.moe_fp8_batched_workspace_bytes(4, 16, 256, 256)
+    f = lib.moe_fp8_batched_experts
+    base = [vp(0x10000 * (i + 1)) for i in range(6)] + [4, 16, 256, 256, vp(0x900000),
+                                                         vp(0x7000000000), n, None]
+    a = list(base); a[6] = 0; assert f(*a) == -2
+    a = list(base); a[9] = 200; assert f(*a) == -2             # I not a multiple of 128
+    a = list(base); a[1] = None; assert f(*a) == -1
+    a = list(base); a[12] = n - 1; assert f(*a) == -4
+    a = list(base); a[1] = vp(0x20002); assert f(*a) == -3     # counts misaligned
+    a = list(base); a[10] = vp(0x10000 + 64); assert f(*a) == -6   # out overlaps x
