@@ -546,6 +546,10 @@ constexpr int kRingW = 256 * 128;      // 256 weight rows x one 128-byte K block
 // fold.  The stage holds the exponent words of the 128 token rows (as the
 // float scales would) and of the tile's 256 weight rows, loaded by waves 2-5
 // in the slots the other waves leave unused.
+//
+// As in GEMM1, a wave whose 64 token rows of the tile are all padding (its
+// first row is the sentinel) loads, waits and stores as usual but skips its
+// MFMAs; its stores write zeros into padding rows, which nothing reads.
 constexpr int kPf2Loads = 7;               // DMA instructions per wave per stage
 constexpr int kPf2Stores = 16;             // output stores per wave per tile
 constexpr int kPf2S = 2048;                // token scales, eight 256-byte wave slots
@@ -660,6 +664,7 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   int s = 0;
   for (int ti = 0; ti < ntile; ++ti) {
     const int nf = 256 * cur.j + 64 * wf;
+    const bool live = load_uniform(args.sorted_ids + cur.b * BM + 64 * wt) < args.P;
     const float* wsp = kMx ? nullptr
                            : args.w_scale + ((size_t)cur.e * (N >> 7) + ((nf < N ? nf : 0) >> 7)) * nkb;
     v4f acc[4][4];
@@ -679,6 +684,7 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
         if (kb + 2 < nkb_t) issue((s + 2) % kRingStages, cur, cwo, kb + 2);
         else issue((s + 2) % kRingStages, nxt, nwo, kb + 2 - nkb_t);
       }
+      if (!live) continue;
       const uint8_t* st = ring + (s % kRingStages) * kStage;
       v8i pf[4];
 #pragma unroll
@@ -771,6 +777,10 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
 // relative error of a few 1e-7, far below one e4m3 step of a.  Operands stay
 // e4m3 in a three-stage LDS ring filled by direct global->LDS loads (XOR
 // swizzle on 16-byte chunks, no bank conflicts on the 16-byte reads).
+// Padding rows sit at the end of an expert's last block, so a wave whose 64
+// token rows start with the sentinel has no real row: it still loads its
+// share of every stage and meets every barrier, but skips its conversions,
+// MFMAs and folds (its rows' outputs are never read).
 constexpr int kPf1Stages = 3;
 constexpr int kPf1W = 256 * 128, kPf1A = 128 * 128, kPf1S = 2048;
 constexpr int kPf1Stage = kPf1W + kPf1A + kPf1S;
@@ -790,6 +800,7 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
   const int e = load_uniform(args.expert_ids + b);
   const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * j;
   const int row0 = b * BM;
+  const bool live = load_uniform(args.sorted_ids + row0 + 64 * wt) < args.P;
 
   // this lane's share of a stage: 4 x 16 bytes of weights, 2 x 16 of tokens
   const uint8_t* wsrc[4];
@@ -862,6 +873,7 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
     if (kb + 1 < nkb) wait_vmem<kPf1Loads>(); else wait_vmem<0>();
     barrier_raw();
     if (kb + 2 < nkb) issue((kb + 2) % kPf1Stages, kb + 2);
+    if (!live) continue;
     const uint8_t* st = ring + (kb % kPf1Stages) * kPf1Stage;
     const float swg = load_uniform(wsg + kb), swu = load_uniform(wsu + kb);
     float sa[4];
