@@ -39,12 +39,12 @@ STAGE_PEAK = {"gemm1": MFMA_F16_PEAK, "gemm2": MFMA_FP8_PEAK}
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
 # kernel source they were taken on: bench reports null traffic once
 # gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "c87e73ea881b192fe9a1f7c0b97d8057bb123a91ef3cd9c98831ea90e842dd18"
+TRAFFIC_SOURCE_SHA256 = "6707406ace4fdffe17133ddf3b09b04ec3fff86c55c35c0d8941244a405d562b"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
-    "prefill.gemm1": (8866069823, 181941227),
-    "prefill.gemm2": (4460599191, 1207437397),
-    "decode.gemm1": (4795508270, 5724960),
-    "decode.gemm2": (2408634871, 7340267),
+    "prefill.gemm1": (10750344255, 184535765),
+    "prefill.gemm2": (4419159031, 1207734795),
+    "decode.gemm1": (4795606118, 5720736),
+    "decode.gemm2": (2408613527, 7340363),
 }
 
 
