@@ -36,7 +36,7 @@ exponent indexing), exponent covariance and the unquantised product.
 
 import numpy as np
 
-from . import e4m3, quant
+from . import quant
 from .moe import bf16_round
 
 
@@ -52,14 +52,7 @@ def block_fp8_linear(x, w, w_scale):
     return bf16_round(acc), {"xq": xq, "xs": xs, "acc": acc}
 
 
-def mx_dequant(q, e, block: int = 32) -> np.ndarray:
-    """uint8 codes [R, K], UE8M0 exponent bytes [R, K/block] -> float64
-    [R, K] with value dec(q[r, k]) * 2^(e[r, k // block] - 127)."""
-    q = np.asarray(q, dtype=np.uint8)
-    R, K = q.shape
-    d = e4m3.decode(q).reshape(R, K // block, block)
-    p = np.ldexp(1.0, np.asarray(e, dtype=np.int64) - 127)
-    return (d * p[:, :, None]).reshape(R, K)
+mx_dequant = quant.mx_dequant
 
 
 def mxfp8_linear(x, w, w_e):

@@ -86,9 +86,26 @@ def expert_ffn(x_rows, w13_e, w13s_e, w2_e, w2s_e):
     return {"xq": xq, "xs": xs, "h": h, "a": a, "aq": aq, "as": as_, "y": y}
 
 
+def expert_ffn_mx(x_rows, w13_e, w13x_e, w2_e, w2x_e):
+    """Steps 2-7 with MXFP8 operands (fp8 oracle API page: block shape
+    [1, 32], uint8 UE8M0 scales, activations through the MXFP8 activation
+    quant): x and the requantised activation are quantised per row and 32
+    columns with power-of-two scales (quant.per_token_group_quant_pow2), the
+    weights carry one UE8M0 exponent per row and 32 K elements (w13x_e
+    [2I, H/32], w2x_e [H, I/32]).  Otherwise as expert_ffn."""
+    x_rows = np.asarray(x_rows, dtype=np.float32)
+    I = w2_e.shape[1]
+    xq, _, xe = quant.per_token_group_quant_pow2(x_rows, 32)
+    h = quant.mx_dequant(xq, xe) @ quant.mx_dequant(w13_e, w13x_e).T
+    a = (silu(h[:, :I]) * h[:, I:]).astype(np.float32)
+    aq, _, ae = quant.per_token_group_quant_pow2(a, 32)
+    y = quant.mx_dequant(aq, ae) @ quant.mx_dequant(w2_e, w2x_e).T
+    return {"xq": xq, "xs": xe, "h": h, "a": a, "aq": aq, "as": ae, "y": y}
+
+
 def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
                 renormalize: bool, tokens=None, num_expert_group=1, topk_group=1,
-                expert_map=None):
+                expert_map=None, mx=False):
     """Whole-layer forward.
 
     x float32 [T, H] (bf16 values), logits float32 [T, E],
@@ -107,6 +124,10 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
     zeros are written for such blocks).  The routing weights are those of the
     global routing either way.
 
+    mx=True: the MXFP8 layer (expert_ffn_mx); w13_scale and w2_scale are then
+    the weights' UE8M0 exponent bytes [E, 2I, H/32] and [E, H, I/32], and
+    info's xs / as hold exponent bytes.
+
     Returns (out float32 [n_tok, H] holding bf16 values, info dict with ids,
     w, xq, xs and per-pair a, aq, as, y in pair order p = row * k + j)."""
     x = np.asarray(x, dtype=np.float32)
@@ -123,7 +144,11 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
                                              renormalize)
     else:
         ids, w = router.topk_softmax(logits, top_k, renormalize)
-    xq, xs = quant.per_token_group_quant(x)
+    if mx:
+        xq, _, xs = quant.per_token_group_quant_pow2(x, 32)
+    else:
+        xq, xs = quant.per_token_group_quant(x)
+    ffn = expert_ffn_mx if mx else expert_ffn
 
     P = T * top_k
     flat = ids.reshape(-1)
@@ -134,12 +159,13 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
     y = np.zeros((P, H), dtype=np.float64)
     a = np.zeros((P, I), dtype=np.float32)
     aq = np.zeros((P, I), dtype=np.uint8)
-    as_ = np.zeros((P, I // 128), dtype=np.float32)
+    as_ = (np.zeros((P, I // 32), dtype=np.uint8) if mx
+           else np.zeros((P, I // 128), dtype=np.float32))
     for e in range(E):
         pairs = np.nonzero(flat == e)[0]
         if pairs.size == 0:
             continue
-        r = expert_ffn(x[pairs // top_k], w13[e], w13_scale[e], w2[e], w2_scale[e])
+        r = ffn(x[pairs // top_k], w13[e], w13_scale[e], w2[e], w2_scale[e])
         y[pairs] = r["y"]
         a[pairs] = r["a"]
         aq[pairs] = r["aq"]

@@ -110,3 +110,13 @@ def per_token_group_quant_pow2(x, group: int = GROUP):
     q = e4m3.encode(quot).reshape(M, K)
     ex = (np.frexp(s.astype(np.float64))[1] - 1 + 127).astype(np.uint8)
     return q, s, ex
+
+
+def mx_dequant(q, e, block: int = 32) -> np.ndarray:
+    """uint8 codes [R, K], UE8M0 exponent bytes [R, K/block] -> float64
+    [R, K] with value dec(q[r, k]) * 2^(e[r, k // block] - 127)."""
+    q = np.asarray(q, dtype=np.uint8)
+    R, K = q.shape
+    d = e4m3.decode(q).reshape(R, K // block, block)
+    p = np.ldexp(1.0, np.asarray(e, dtype=np.int64) - 127)
+    return (d * p[:, :, None]).reshape(R, K)

@@ -173,3 +173,23 @@ def make_mx_linear(M, N, K, seed_base, device="cpu", std=WEIGHT_STD):
                     dtype=torch.float32) * std
     wq, we = mx_quantize_e4m3(w)
     return x, wq, we
+
+
+def make_mx_weights(H, I, E, seed, device="cpu", std=WEIGHT_STD):
+    """MXFP8 expert weights: w13 uint8 [E, 2I, H] with UE8M0 exponents
+    [E, 2I, H/32], w2 uint8 [E, H, I] with exponents [E, H, I/32]; the same
+    N(0, std) draws per expert as make_weights, cast with [1, 32] blocks."""
+    if H % BLOCK or I % BLOCK:
+        raise ValueError("H and I must be multiples of 128")
+    w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
+    w13e = torch.empty((E, 2 * I, H // MX_BLOCK), dtype=torch.uint8, device=device)
+    w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
+    w2e = torch.empty((E, H, I // MX_BLOCK), dtype=torch.uint8, device=device)
+    for e in range(E):
+        g = _gen(device, seed * 1_000_003 + e)
+        a = torch.randn((2 * I, H), generator=g, device=device, dtype=torch.float32) * std
+        w13[e], w13e[e] = mx_quantize_e4m3(a)
+        a = torch.randn((H, I), generator=g, device=device, dtype=torch.float32) * std
+        w2[e], w2e[e] = mx_quantize_e4m3(a)
+        del a
+    return w13, w13e, w2, w2e

@@ -272,3 +272,70 @@ def test_batched_experts_rows_are_independent():
     outp, _ = moe.batched_experts(xp, counts, *ws)
     assert np.array_equal(outp[2, :4], out[2, perm])
     assert np.array_equal(outp[0], out[0])
+
+
+# ---- MXFP8 layer ([1, 32] blocks, power-of-two scales) ----
+
+def _mx_brute_quant(rows):
+    """Scalar reference of the group-32 power-of-two quantiser: float64
+    dequantised values (exact log2 for the scale, exhaustive nearest code)."""
+    import math
+    out = np.zeros(rows.shape)
+    for r in range(rows.shape[0]):
+        for g in range(rows.shape[1] // 32):
+            vals = [np.float32(v) for v in rows[r, 32 * g:32 * (g + 1)]]
+            amax = max(abs(v) for v in vals)
+            s32 = np.float32(max(amax, np.float32(1e-8))) / np.float32(448)
+            p = 2.0 ** math.ceil(math.log2(float(s32)))
+            for i, v in enumerate(vals):
+                c = _brute.nearest_code(np.float32(v / np.float32(p)))
+                out[r, 32 * g + i] = float(torch.tensor([c], dtype=torch.uint8).view(torch.float8_e4m3fn).double()) * p
+    return out
+
+
+def _mx_weights_torch(q, e):
+    """float64 weights from codes and UE8M0 bytes through torch's float8 cast."""
+    d = torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).double()
+    ex = torch.from_numpy(np.asarray(e, np.int64) - 127).repeat_interleave(32, dim=1)
+    return torch.ldexp(d, ex).numpy()
+
+
+def test_mx_single_expert_is_a_brute_force_gated_mlp():
+    from synth import make_mx_weights
+    H, I, T = 128, 128, 3
+    x, logits = make_activations(H, 1, T, seed_base=931)
+    w13, w13e, w2, w2e = [a.numpy() for a in make_mx_weights(H, I, 1, 932)]
+    out, info = moe.moe_forward(x.float().numpy(), logits.numpy(), w13, w13e, w2, w2e, 1, True,
+                                mx=True)
+    xf = _mx_brute_quant(x.float().numpy())
+    h = xf @ _mx_weights_torch(w13[0], w13e[0]).T
+    a = (h[:, :I] / (1.0 + np.exp(-h[:, :I])) * h[:, I:]).astype(np.float32)
+    y = _mx_brute_quant(a) @ _mx_weights_torch(w2[0], w2e[0]).T
+    np.testing.assert_allclose(info["a"], a, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(info["y"], y, rtol=1e-9, atol=1e-12)
+    assert np.array_equal(out, moe.bf16_round(y))
+
+
+def test_mx_layer_loosely_matches_the_unquantised_mlp():
+    from synth import WEIGHT_STD, mx_quantize_e4m3
+    H, I, E, k, T = 256, 256, 4, 2, 8
+    x, logits = make_activations(H, E, T, seed_base=941)
+    g = torch.Generator().manual_seed(942)
+    wf13 = torch.randn((E, 2 * I, H), generator=g) * WEIGHT_STD
+    wf2 = torch.randn((E, H, I), generator=g) * WEIGHT_STD
+    q = [mx_quantize_e4m3(wf13[e]) for e in range(E)]
+    r = [mx_quantize_e4m3(wf2[e]) for e in range(E)]
+    w13 = np.stack([a.numpy() for a, _ in q]); w13e = np.stack([b.numpy() for _, b in q])
+    w2 = np.stack([a.numpy() for a, _ in r]); w2e = np.stack([b.numpy() for _, b in r])
+    out, info = moe.moe_forward(x.float().numpy(), logits.numpy(), w13, w13e, w2, w2e, k, True,
+                                mx=True)
+    xd = x.double().numpy()
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = int(info["ids"][t, j])
+            h = wf13[e].double().numpy() @ xd[t]
+            a = h[:I] / (1 + np.exp(-h[:I])) * h[I:]
+            ref[t] += float(info["w"][t, j]) * (wf2[e].double().numpy() @ a)
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel < 0.1, rel
