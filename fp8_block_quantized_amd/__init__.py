@@ -30,6 +30,7 @@ EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layo
            "moe_fp8_forward", "moe_fp8_forward_traced", "per_token_group_quant_fp8",
            "per_token_group_quant_fp8_fmt", "moe_topk_softmax", "moe_topk_softmax_grouped",
            "moe_fp8_forward_routed", "moe_fp8_batched_workspace_bytes", "moe_fp8_batched_experts",
+           "moe_fp8_mx_workspace_bytes", "moe_fp8_mx_workspace_layout", "moe_fp8_mx_forward",
            "moe_align_scratch_bytes", "moe_align", "moe_status_string",
            "fp8_block_linear_workspace_bytes", "fp8_block_linear",
            "mxfp8_linear_workspace_bytes", "mxfp8_linear"]
@@ -78,6 +79,12 @@ def load_library(path=LIB_PATH):
     lib.moe_fp8_batched_workspace_bytes.restype = c_size
     lib.moe_fp8_batched_experts.argtypes = [vp] * 6 + [c_int] * 4 + [vp, vp, c_size, vp]
     lib.moe_fp8_batched_experts.restype = c_int
+    lib.moe_fp8_mx_workspace_bytes.argtypes = [c_int] * 5
+    lib.moe_fp8_mx_workspace_bytes.restype = c_size
+    lib.moe_fp8_mx_workspace_layout.argtypes = [c_int] * 5 + [ctypes.POINTER(c_size)]
+    lib.moe_fp8_mx_workspace_layout.restype = c_int
+    lib.moe_fp8_mx_forward.argtypes = [vp] * 6 + [c_int] * 6 + [vp, vp, c_size, vp]
+    lib.moe_fp8_mx_forward.restype = c_int
     lib.moe_align_scratch_bytes.argtypes = [c_int] * 3
     lib.moe_align_scratch_bytes.restype = c_size
     lib.moe_align.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]
@@ -126,10 +133,10 @@ def moe_fp8_workspace_bytes(T, H, I, E, top_k):
     return load_library().moe_fp8_workspace_bytes(T, H, I, E, top_k)
 
 
-def moe_fp8_workspace_layout(T, H, I, E, top_k):
+def moe_fp8_workspace_layout(T, H, I, E, top_k, mx=False):
     offs = (ctypes.c_size_t * len(TAPS))()
-    _check("moe_fp8_workspace_layout",
-           load_library().moe_fp8_workspace_layout(T, H, I, E, top_k, offs))
+    fn = "moe_fp8_mx_workspace_layout" if mx else "moe_fp8_workspace_layout"
+    _check(fn, getattr(load_library(), fn)(T, H, I, E, top_k, offs))
     return dict(zip(TAPS, list(offs)))
 
 
@@ -197,10 +204,11 @@ def moe_fp8_forward_routed(x, router_logits, w13, w13_scale, w2, w2_scale, top_k
     return out
 
 
-def workspace_taps(workspace, T, H, I, E, top_k):
-    """Views of the forward's intermediates inside its workspace."""
-    off = moe_fp8_workspace_layout(T, H, I, E, top_k)
-    bm = moe_fp8_block_m(T, H, I, E, top_k)
+def workspace_taps(workspace, T, H, I, E, top_k, mx=False):
+    """Views of the forward's intermediates inside its workspace (mx: the
+    MXFP8 layer's, block_m 128 and exponent bytes in xs / as)."""
+    off = moe_fp8_workspace_layout(T, H, I, E, top_k, mx)
+    bm = 128 if mx else moe_fp8_block_m(T, H, I, E, top_k)
     P = T * top_k
     cap = -(-(P + E * (bm - 1)) // bm) * bm
 
@@ -220,9 +228,9 @@ def workspace_taps(workspace, T, H, I, E, top_k):
         "ntpp": view("ntpp", torch.int32, (1,)),
         "pair_pos": view("pair_pos", torch.int32, (P,)),
         "xq": view("xq", torch.uint8, (T, H)),
-        "xs": view("xs", torch.float32, (T, H // 128)),
+        "xs": view("xs", torch.uint8, (T, H // 32)) if mx else view("xs", torch.float32, (T, H // 128)),
         "aq": view("aq", torch.uint8, (cap, I)),
-        "as": view("as", torch.float32, (cap, I // 128)),
+        "as": view("as", torch.uint8, (cap, I // 32)) if mx else view("as", torch.float32, (cap, I // 128)),
         "y": view("y", torch.bfloat16, (cap, -(-H // 256) * 256)),
     }
 
@@ -386,4 +394,32 @@ def moe_fp8_batched_experts(x, expert_num_tokens, w13, w13_scale, w2, w2_scale, 
         E, M, H, I, _dev(out, torch.bfloat16, "out"), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream))
     _check("moe_fp8_batched_experts", st)
+    return out
+
+
+def moe_fp8_mx_workspace_bytes(T, H, I, E, top_k):
+    return load_library().moe_fp8_mx_workspace_bytes(T, H, I, E, top_k)
+
+
+def moe_fp8_mx_forward(x, router_logits, w13, w13_scale, w2, w2_scale, top_k, renormalize,
+                       out=None, workspace=None, stream=None):
+    """MXFP8 MoE forward: w13 uint8 [E, 2I, H] with UE8M0 bytes [E, 2I, H/32],
+    w2 uint8 [E, H, I] with UE8M0 bytes [E, H, I/32]."""
+    T, H = x.shape
+    E = router_logits.shape[1]
+    I = w2.shape[2]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        n = moe_fp8_mx_workspace_bytes(T, H, I, E, top_k)
+        if n == 0:
+            raise MoeError("moe_fp8_mx_workspace_bytes", -2)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    st = load_library().moe_fp8_mx_forward(
+        _dev(x, torch.bfloat16, "x"), _dev(router_logits, torch.float32, "router_logits"),
+        _dev(w13, torch.uint8, "w13"), _dev(w13_scale, torch.uint8, "w13_scale"),
+        _dev(w2, torch.uint8, "w2"), _dev(w2_scale, torch.uint8, "w2_scale"),
+        T, H, I, E, int(top_k), int(bool(renormalize)), _dev(out, torch.bfloat16, "out"),
+        _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check("moe_fp8_mx_forward", st)
     return out

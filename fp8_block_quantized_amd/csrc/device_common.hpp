@@ -56,6 +56,12 @@ __device__ __forceinline__ void group_scale(float amax, float& s, float& r) {
   r = 1.0f / s;
 }
 
+// float32 s > 0 (normal) -> the smallest power of two >= s, as its bits.
+__device__ __forceinline__ uint32_t ceil_pow2_bits(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return (b & 0x7FFFFFu) ? (b & 0x7F800000u) + 0x00800000u : b;
+}
+
 // Four e4m3fn codes (one dword) -> four f16 values, exactly (every e4m3fn
 // value is an f16 value; the hardware conversion scales by 1.0).
 __device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, _Float16* out) {

@@ -944,6 +944,164 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
   }
 }
 
+// GEMM1 of the MXFP8 layer (fp8 oracle API page, block shape [1, 32] with
+// UE8M0 scales): xq and w13 carry one power-of-two exponent per row and 32 K
+// elements, which v_mfma_scale_f32_16x16x128_f8f6f4 applies itself, so the
+// float32 accumulator runs through the MFMAs across K blocks (the lane that
+// holds a row's 32 K values in the instruction's K order, chunks g and g + 4
+// of the block, passes that row's exponent of block g).  The epilogue forms
+// a = silu(gate) * up in float32 and requantises it in groups of 32 features
+// with power-of-two scales: a wave holds the 32 gate and 32 up rows of one
+// group (features 32 wf .. 32 wf + 31 of the tile), so the group maximum of
+// a token is a two-step butterfly over its four lanes.  Tile, ring and row
+// gather as in moe_gemm1_pf_kernel; the stage's exponent slots hold the 128
+// token rows' words (waves 0, 1) and the 256 weight rows' words (waves 2-5).
+// As there, a wave whose 64 token rows are all padding skips its MFMAs.
+__global__ __launch_bounds__(512) void moe_gemm1_mx_kernel(GemmArgs args) {
+  constexpr int BM = 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kPf1Stages * kPf1Stage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 2, wf = wave & 3;
+  const int g = lane >> 4, l16 = lane & 15;
+  const TileCoord tc = tile_of(blockIdx.x, args);
+  if (!tc.valid) return;
+  const int b = tc.b, j = tc.j;
+  const int e = load_uniform(args.expert_ids + b);
+  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * j;
+  const int row0 = b * BM;
+  const bool live = load_uniform(args.sorted_ids + row0 + 64 * wt) < args.P;
+  // w13 row of tile row r: gate rows i0 .. i0 + 127, then up rows I + i0 ..
+  auto wrow_of = [&](int r) { return r < 128 ? i0 + r : I + i0 + (r - 128); };
+
+  const uint8_t* wsrc[4];
+  const uint8_t* asrc[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = (wave * 4 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+    wsrc[i] = args.w + ((size_t)e * args.N + wrow_of(r)) * K + lc * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pos = (wave * 2 + i) * 64 + lane, r = pos >> 3, lc = (pos & 7) ^ (r & 7);
+    const int p = args.sorted_ids[row0 + r];
+    asrc[i] = args.act + (size_t)(p < args.P ? p / args.top_k : 0) * K + lc * 16;
+  }
+  // exponent words (4 blocks of 32 per K block): token rows for waves 0, 1 (6, 7
+  // repeat them into unused slots), weight tile rows 64 (wave - 2) + lane for 2-5
+  const uint32_t* esrc;
+  if (wave >= 2 && wave < 6) {
+    esrc = (const uint32_t*)args.w_scale + ((size_t)e * args.N + wrow_of(64 * (wave - 2) + lane)) * nkb;
+  } else {
+    const int p = args.sorted_ids[row0 + (wave & 1) * 64 + lane];
+    esrc = (const uint32_t*)args.act_scale + (size_t)(p < args.P ? p / args.top_k : 0) * nkb;
+  }
+  auto issue = [&](int stage, int kb) {
+    const uint32_t base = lds_offset(ring + stage * kPf1Stage);
+    const size_t ko = (size_t)kb * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(wsrc[i] + ko, base + (wave * 4 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(asrc[i] + ko, base + kPf1W + (wave * 2 + i) * 1024);
+    dma4(esrc + kb, base + kPf1W + kPf1A + wave * 256);
+  };
+  // tile rows of this wave's weight fragments: gate 32 wf + 16 pp, up 128 + 32 wf + 16 (pp - 2)
+  int prow[4], pw[4][2], pa[4][2];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    prow[pp] = (pp < 2 ? 32 * wf + 16 * pp : 128 + 32 * wf + 16 * (pp - 2)) + l16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pw[pp][h] = prow[pp] * 128 + (((g + 4 * h) ^ (l16 & 7)) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 64 * wt + 16 * q + l16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pa[q][h] = kPf1W + r * 128 + (((g + 4 * h) ^ (l16 & 7)) << 4);
+  }
+  v4f acc[4][4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  if (nkb > 1) issue(1, 1);
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) wait_vmem<kPf1Loads>(); else wait_vmem<0>();
+    barrier_raw();
+    if (kb + 2 < nkb) issue((kb + 2) % kPf1Stages, kb + 2);
+    if (!live) continue;
+    const uint8_t* st = ring + (kb % kPf1Stages) * kPf1Stage;
+    const uint8_t* se = st + kPf1W + kPf1A;
+    v8i pf[4];
+    int ew[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const uint4 a0 = *(const uint4*)(st + pw[pp][0]);
+      const uint4 a1 = *(const uint4*)(st + pw[pp][1]);
+      pf[pp] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      ew[pp] = se[512 + prow[pp] * 4 + g];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 b0 = *(const uint4*)(st + pa[q][0]);
+      const uint4 b1 = *(const uint4*)(st + pa[q][1]);
+      const v8i bq = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      const int ea = se[(64 * wt + 16 * q + l16) * 4 + g];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp)
+        acc[pp][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf[pp], bq, acc[pp][q], 0, 0, 0,
+                                                                     ew[pp], 0, ea);
+    }
+  }
+
+  // a = silu(gate) * up, requantised per token and group of 32 features:
+  // lane (g, l16) holds features 32 wf + 16 pg + 4 g + r (pg, r < 2, 4) of token row
+  // 64 wt + 16 q + l16; the group's other features sit in the lanes g' != g
+  uint8_t* ae = (uint8_t*)args.as_out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float av[2][4];
+    float m = 0.0f;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gt = acc[pg][q][r], up = acc[pg + 2][q][r];
+        av[pg][r] = gt / (1.0f + expf(-gt)) * up;
+        m = __builtin_fmaxf(m, __builtin_fabsf(av[pg][r]));
+      }
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+    const uint32_t sb = ceil_pow2_bits(__builtin_fmaxf(m, kAmaxEps) / kFp8Max);
+    const float rcp = __uint_as_float((254u - (sb >> 23)) << 23);   // exactly 1 / scale
+    const size_t grow = (size_t)(row0 + 64 * wt + 16 * q + l16);
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const uint32_t word = pack4_e4m3(clamp_fp8(av[pg][0] * rcp), clamp_fp8(av[pg][1] * rcp),
+                                       clamp_fp8(av[pg][2] * rcp), clamp_fp8(av[pg][3] * rcp));
+      *(uint32_t*)(args.aq_out + grow * I + i0 + 32 * wf + 16 * pg + 4 * g) = word;
+    }
+    if (g == 0) ae[grow * (I >> 5) + ((i0 + 32 * wf) >> 5)] = (uint8_t)(sb >> 23);
+  }
+}
+
+hipError_t launch_gemm1_mx(const uint8_t* xq, const uint8_t* xe, const uint8_t* w13,
+                           const uint8_t* w13e, const int32_t* sorted_ids, const int32_t* expert_ids,
+                           const int32_t* ntpp, const int32_t* eoff, int E, int H, int I, int P,
+                           int top_k, int nblk, uint8_t* aq, uint8_t* ae, hipStream_t stream) {
+  GemmArgs a{};
+  a.eoff = eoff; a.E = E; a.split = 1;
+  a.act = xq; a.act_scale = (const float*)xe; a.w = w13; a.w_scale = (const float*)w13e;
+  a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
+  a.aq_out = aq; a.as_out = (float*)ae;
+  a.K = H; a.N = 2 * I; a.I = I; a.H = H; a.P = P; a.top_k = top_k;
+  a.nblk = nblk; a.n_tiles = I / 128; a.mx = 1;
+  hipLaunchKernelGGL(moe_gemm1_mx_kernel, dim3((unsigned)(nblk * a.n_tiles)), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
 // Sum of the float32 K-slice partials in slice order, rounded once to bf16:
 // out[r, c] = bf16( sum_s part[s, r, c] ) for r < rows, c < cols (cols % 8 == 0).
 __global__ __launch_bounds__(256) void reduce_slices_kernel(const float4* __restrict__ part,
@@ -1051,6 +1209,21 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
   a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
   a.n_tiles = (H + 255) / 256; a.nblk = nblk;
   return launch_gemm2_bm(a, BM, stream);
+}
+
+hipError_t launch_gemm2_mx(const uint8_t* aq, const uint8_t* ae, const uint8_t* w2, const uint8_t* w2e,
+                           const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
+                           const int32_t* eoff, int E, int H, int I, int P, int nblk, uint16_t* y,
+                           int y_stride, hipStream_t stream) {
+  GemmArgs a{};
+  a.eoff = eoff; a.E = E; a.split = 1; a.mx = 1;
+  a.act = aq; a.act_scale = (const float*)ae; a.w = w2; a.w_scale = (const float*)w2e;
+  a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
+  a.y_out = y; a.y_stride = y_stride;
+  a.y_rows = nblk * 128; a.y_cols = y_stride; a.y_dump = y; a.ksplit = 1;
+  a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
+  a.n_tiles = (H + 255) / 256; a.nblk = nblk;
+  return launch_gemm2_bm(a, 128, stream);
 }
 
 hipError_t launch_gemm2_bounded(const uint8_t* act, const float* act_scale, const uint8_t* w,

@@ -44,9 +44,12 @@ struct Layout {
   size_t total;
 };
 
-void make_layout(int T, int H, int I, int E, int top_k, Layout& L) {
+// block_m 0: the forward's choice; the MXFP8 layer passes 128.  The
+// activation scale regions hold float32 per 128 elements or, at the same
+// size, exponent bytes per 32.
+void make_layout(int T, int H, int I, int E, int top_k, Layout& L, int block_m = 0) {
   const size_t P = (size_t)T * top_k;
-  L.BM = pick_block_m(T, E, top_k);
+  L.BM = block_m ? block_m : pick_block_m(T, E, top_k);
   L.cap = round_up(P + (size_t)E * (L.BM - 1), L.BM);
   size_t sz[MOE_TAP_COUNT];
   sz[MOE_TAP_TOPK_IDS] = P * 4;
@@ -360,6 +363,82 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, con
                         (int)y_stride(H), stream))
     return MOE_ERR_HIP;
   if (moe::launch_combine(y, (int)y_stride(H), ppos, nullptr, T, H, 1, (uint16_t*)out, stream))
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+size_t moe_fp8_mx_workspace_bytes(int T, int H, int I, int E, int top_k) {
+  if (check_moe_shape(T, H, I, E, top_k) != MOE_OK || I < 256) return 0;
+  Layout L;
+  make_layout(T, H, I, E, top_k, L, 128);
+  return L.total;
+}
+
+int moe_fp8_mx_workspace_layout(int T, int H, int I, int E, int top_k,
+                                size_t offsets[MOE_TAP_COUNT]) {
+  if (!offsets) return MOE_ERR_NULL;
+  const int st = check_moe_shape(T, H, I, E, top_k);
+  if (st != MOE_OK) return st;
+  if (I < 256) return MOE_ERR_UNSUPPORTED;
+  Layout L;
+  make_layout(T, H, I, E, top_k, L, 128);
+  for (int i = 0; i < MOE_TAP_COUNT; ++i) offsets[i] = L.off[i];
+  return MOE_OK;
+}
+
+int moe_fp8_mx_forward(const void* x, const float* router_logits, const uint8_t* w13,
+                       const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, int T,
+                       int H, int I, int E, int top_k, int renormalize, void* out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !router_logits || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace)
+    return MOE_ERR_NULL;
+  int st = check_moe_shape(T, H, I, E, top_k);
+  if (st != MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1) return MOE_ERR_SHAPE;
+  if (I < 256) return MOE_ERR_UNSUPPORTED;
+  Layout L;
+  make_layout(T, H, I, E, top_k, L, 128);
+  if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)x % 16 || (uintptr_t)out % 16 || (uintptr_t)w13 % 16 || (uintptr_t)w2 % 16 ||
+      (uintptr_t)router_logits % 4 || (uintptr_t)w13_scale % 4 || (uintptr_t)w2_scale % 4)
+    return MOE_ERR_UNSUPPORTED;
+  const size_t out_bytes = (size_t)T * H * 2;
+  const size_t w13_bytes = (size_t)E * 2 * I * H, w2_bytes = (size_t)E * H * I;
+  if (overlaps(out, out_bytes, x, out_bytes) ||
+      overlaps(out, out_bytes, router_logits, (size_t)T * E * 4) ||
+      overlaps(out, out_bytes, w13, w13_bytes) || overlaps(out, out_bytes, w2, w2_bytes) ||
+      overlaps(out, out_bytes, w13_scale, w13_bytes / 32) ||
+      overlaps(out, out_bytes, w2_scale, w2_bytes / 32) ||
+      overlaps(out, out_bytes, workspace, L.total))
+    return MOE_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  int32_t* ids = (int32_t*)(ws + L.off[MOE_TAP_TOPK_IDS]);
+  float* tw = (float*)(ws + L.off[MOE_TAP_TOPK_WEIGHTS]);
+  int32_t* sorted = (int32_t*)(ws + L.off[MOE_TAP_SORTED_IDS]);
+  int32_t* eids = (int32_t*)(ws + L.off[MOE_TAP_EXPERT_IDS]);
+  int32_t* ntpp = (int32_t*)(ws + L.off[MOE_TAP_NTPP]);
+  int32_t* ppos = (int32_t*)(ws + L.off[MOE_TAP_PAIR_POS]);
+  uint8_t* xq = (uint8_t*)(ws + L.off[MOE_TAP_XQ]);
+  uint8_t* xe = (uint8_t*)(ws + L.off[MOE_TAP_XS]);
+  uint8_t* aq = (uint8_t*)(ws + L.off[MOE_TAP_AQ]);
+  uint8_t* ae = (uint8_t*)(ws + L.off[MOE_TAP_AS]);
+  uint16_t* y = (uint16_t*)(ws + L.off[MOE_TAP_Y]);
+  void* scratch = ws + L.off[MOE_TAP_ALIGN_SCRATCH];
+  const int P = T * top_k;
+  const int nblk = (int)(L.cap / L.BM);
+  if (moe::launch_topk_softmax(router_logits, T, E, top_k, renormalize, 1, 1, ids, tw, stream))
+    return MOE_ERR_HIP;
+  if (moe::launch_align(ids, nullptr, 0, P, E, L.BM, sorted, eids, ntpp, ppos, scratch, stream))
+    return MOE_ERR_HIP;
+  if (moe::launch_group_quant_fmt(x, T, H, 32, moe::kScaleUe8m0, xq, xe, stream)) return MOE_ERR_HIP;
+  const int32_t* eoff = moe::align_expert_offsets(scratch, P, E);
+  if (moe::launch_gemm1_mx(xq, xe, w13, w13_scale, sorted, eids, ntpp, eoff, E, H, I, P, top_k, nblk,
+                           aq, ae, stream))
+    return MOE_ERR_HIP;
+  if (moe::launch_gemm2_mx(aq, ae, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, P, nblk, y,
+                           (int)y_stride(H), stream))
+    return MOE_ERR_HIP;
+  if (moe::launch_combine(y, (int)y_stride(H), ppos, tw, T, H, top_k, (uint16_t*)out, stream))
     return MOE_ERR_HIP;
   return MOE_OK;
 }

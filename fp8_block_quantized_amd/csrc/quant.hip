@@ -25,12 +25,6 @@
 
 namespace moe {
 
-// float32 s > 0 (normal) -> the smallest power of two >= s, as its bits.
-__device__ __forceinline__ uint32_t ceil_pow2_bits(float s) {
-  const uint32_t b = __float_as_uint(s);
-  return (b & 0x7FFFFFu) ? (b & 0x7F800000u) + 0x00800000u : b;
-}
-
 // kMasked: the rows form E blocks of M rows (blockIdx.y = block e) of which
 // only the first counts[e] are quantised (the batched expert format); the
 // others are neither read nor written.

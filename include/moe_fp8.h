@@ -200,6 +200,43 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens,
                             void* out, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/*
+ * The MXFP8 MoE layer forward: the fp8 oracle API page's MXFP8 quant config,
+ * block shape [1, 32] with uint8 UE8M0 scales, whose activations go through
+ * the MXFP8 activation quant:
+ *   (ids, w) = softmax top-k of router_logits (as moe_fp8_forward)
+ *   (xq, xe) = per_token_group_quant_fp8_fmt(x, group 32, MOE_SCALE_UE8M0)
+ *   h = sum_k dec(xq)*2^(xe-127) * dec(w13[e])*2^(w13_scale[e]-127)   per [1, 32] block
+ *   a = silu(h[:, :I]) * h[:, I:], requantised per token and 32 features with
+ *       power-of-two scales (UE8M0)
+ *   y = the same block-scaled product of a with w2[e]
+ *   out[t] = bf16( sum over the top_k slots of w * y )
+ * Both GEMMs run on FP8 MFMAs that apply the exponents in hardware
+ * (float32 accumulation), the block size is always 128.
+ *
+ *   x             bf16    [T, H]
+ *   router_logits float32 [T, E]
+ *   w13           e4m3fn  [E, 2I, H]      rows [0, I) gate, [I, 2I) up
+ *   w13_scale     uint8   [E, 2I, H/32]   UE8M0 exponent bytes (4-byte aligned)
+ *   w2            e4m3fn  [E, H, I]
+ *   w2_scale      uint8   [E, H, I/32]
+ *   out           bf16    [T, H]; must not overlap any input or the workspace
+ *   workspace     moe_fp8_mx_workspace_bytes() bytes, 256-byte aligned; its
+ *                 MOE_TAP_* tensors at moe_fp8_mx_workspace_layout()'s offsets
+ *                 (MOE_TAP_XS and MOE_TAP_AS hold exponent bytes [rows, K/32])
+ * Constraints: those of moe_fp8_forward, and I >= 256 (else
+ * MOE_ERR_UNSUPPORTED; the workspace query returns 0).
+ */
+size_t moe_fp8_mx_workspace_bytes(int T, int H, int I, int E, int top_k);
+int moe_fp8_mx_workspace_layout(int T, int H, int I, int E, int top_k,
+                                size_t offsets[MOE_TAP_COUNT]);
+int moe_fp8_mx_forward(const void* x, const float* router_logits,
+                       const uint8_t* w13, const uint8_t* w13_scale,
+                       const uint8_t* w2, const uint8_t* w2_scale,
+                       int T, int H, int I, int E, int top_k, int renormalize,
+                       void* out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* Stages of the forward, in launch order (for moe_fp8_forward_traced). */
 enum {
   MOE_STAGE_ROUTER = 0,     /* softmax top-k */

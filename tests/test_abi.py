@@ -248,3 +248,21 @@ def test_batched_argument_checks():
     a = list(base); a[12] = n - 1; assert f(*a) == -4
     a = list(base); a[1] = vp(0x20002); assert f(*a) == -3     # counts misaligned
     a = list(base); a[10] = vp(0x10000 + 64); assert f(*a) == -6   # out overlaps x
+
+
+def test_mx_forward_argument_checks():
+    # every call below is invalid, so it returns before anything is launched
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    T, H, I, E, k = 4, 256, 256, 8, 2
+    n = moe.moe_fp8_mx_workspace_bytes(T, H, I, E, k)
+    assert n > 0 and moe.moe_fp8_mx_workspace_bytes(T, H, 128, E, k) == 0     # I < 256
+    f = lib.moe_fp8_mx_forward
+    base = [vp(0x10000 * (i + 1)) for i in range(6)] + [T, H, I, E, k, 1, vp(0x900000),
+                                                         vp(0x7000000000), n, None]
+    a = list(base); a[8] = 128; assert f(*a) == -3          # I = 128 unsupported
+    a = list(base); a[11] = 2; assert f(*a) == -2           # renormalize not 0/1
+    a = list(base); a[3] = None; assert f(*a) == -1
+    a = list(base); a[14] = n - 1; assert f(*a) == -4
+    a = list(base); a[3] = vp(0x40002); assert f(*a) == -3   # exponents misaligned
+    a = list(base); a[12] = vp(0x10000 + 64); assert f(*a) == -6   # out overlaps x
