@@ -328,6 +328,36 @@ def main():
                     "rows": rows, "ms": bms, "alg_bytes": bbytes, "alg_flops": bflops})
     del bx, bw, bout, bws
 
+    # the MXFP8 layer ([1, 32] blocks, UE8M0 scales, FP8 MFMAs in both GEMMs)
+    # on the same inputs, with the same weights cast to MXFP8
+    from synth import make_mx_weights
+    mxw = make_mx_weights(H, I, E, base + 2, dev)
+    mx_layer = {"workload": f"{args.workload}-shaped MoE layer with MXFP8 weights and activations"}
+    for n in order:
+        ph = phases[n]
+        T = ph["T"]
+        mws = torch.empty(moe.moe_fp8_mx_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True, out=ph["out"], workspace=mws)
+        me = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        me[0].record()
+        for _ in range(args.steps):
+            moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True, out=ph["out"], workspace=mws)
+        me[1].record()
+        torch.cuda.synchronize()
+        mms = me[0].elapsed_time(me[1]) / args.steps
+        ids = moe.workspace_taps(mws, T, H, I, E, k, mx=True)["topk_ids"].cpu().numpy()
+        e_act = int(np.unique(ids).size)
+        mbytes = e_act * (2 * I * H + H * I) * 33 // 32 + 4 * T * H
+        mflops = 6 * T * k * H * I
+        r = roofline_of(mbytes, mflops, mms * 1e-3, MFMA_FP8_PEAK)
+        r.update({"T": T, "ms": mms, "tokens_per_s": T / (mms * 1e-3), "active_experts": e_act,
+                  "alg_bytes": mbytes, "alg_flops": mflops})
+        mx_layer[n] = r
+        del mws
+    del mxw
+
     dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
     dom = kernels[dom_name]
     roof = roofline_of(dom["bytes"], dom["flops"], dom["ms"] * 1e-3, dom["peak"])
@@ -360,6 +390,7 @@ def main():
         "dense_linear": dense,
         "dense_linear_mxfp8": dense_mx,
         "batched_experts": batched,
+        "moe_mxfp8": mx_layer,
     }
     if not args.no_cpu_baseline and "decode" in phases:
         ph = phases["decode"]
