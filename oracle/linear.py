@@ -60,6 +60,6 @@ def mxfp8_linear(x, w, w_e):
     [N, K/32].  Returns (out float32 [M, N] holding bf16 values, info with xq,
     xe and the float64 product before rounding)."""
     x = np.asarray(x, dtype=np.float32)
-    xq, _, xe = quant.per_token_group_quant_pow2(x, 32)
+    xq, _, xe = quant.per_token_group_quant_pow2(x, quant.MX_GROUP)
     acc = mx_dequant(xq, xe) @ mx_dequant(w, w_e).T
     return bf16_round(acc), {"xq": xq, "xe": xe, "acc": acc}

@@ -95,10 +95,10 @@ def expert_ffn_mx(x_rows, w13_e, w13x_e, w2_e, w2x_e):
     [2I, H/32], w2x_e [H, I/32]).  Otherwise as expert_ffn."""
     x_rows = np.asarray(x_rows, dtype=np.float32)
     I = w2_e.shape[1]
-    xq, _, xe = quant.per_token_group_quant_pow2(x_rows, 32)
+    xq, _, xe = quant.per_token_group_quant_pow2(x_rows, quant.MX_GROUP)
     h = quant.mx_dequant(xq, xe) @ quant.mx_dequant(w13_e, w13x_e).T
     a = (silu(h[:, :I]) * h[:, I:]).astype(np.float32)
-    aq, _, ae = quant.per_token_group_quant_pow2(a, 32)
+    aq, _, ae = quant.per_token_group_quant_pow2(a, quant.MX_GROUP)
     y = quant.mx_dequant(aq, ae) @ quant.mx_dequant(w2_e, w2x_e).T
     return {"xq": xq, "xs": xe, "h": h, "a": a, "aq": aq, "as": ae, "y": y}
 
@@ -145,7 +145,7 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
     else:
         ids, w = router.topk_softmax(logits, top_k, renormalize)
     if mx:
-        xq, _, xs = quant.per_token_group_quant_pow2(x, 32)
+        xq, _, xs = quant.per_token_group_quant_pow2(x, quant.MX_GROUP)
     else:
         xq, xs = quant.per_token_group_quant(x)
     ffn = expert_ffn_mx if mx else expert_ffn

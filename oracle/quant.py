@@ -35,6 +35,7 @@ import numpy as np
 from . import e4m3
 
 GROUP = 128
+MX_GROUP = 32          # the MXFP8 [1, 32] block: one UE8M0 scale per 32 elements
 AMAX_EPS = np.float32(1e-8)
 FP8_MAX = np.float32(448.0)
 
@@ -112,7 +113,7 @@ def per_token_group_quant_pow2(x, group: int = GROUP):
     return q, s, ex
 
 
-def mx_dequant(q, e, block: int = 32) -> np.ndarray:
+def mx_dequant(q, e, block: int = MX_GROUP) -> np.ndarray:
     """uint8 codes [R, K], UE8M0 exponent bytes [R, K/block] -> float64
     [R, K] with value dec(q[r, k]) * 2^(e[r, k // block] - 127)."""
     q = np.asarray(q, dtype=np.uint8)

@@ -104,3 +104,17 @@ def test_float32_scales_group_32_brute_force():
         for g in range(4):
             codes, sc = _brute.quant_group_scalar(x[r, 32 * g:32 * (g + 1)])
             assert list(q[r, 32 * g:32 * (g + 1)]) == codes and s[r, g] == sc
+
+
+def test_mx_constants_match_pages():
+    import json
+    import os
+    from synth import MX_BLOCK
+    with open(os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")) as f:
+        c = json.load(f)
+    assert [1, quant.MX_GROUP] == c["mxfp8_block"]["value"] and MX_BLOCK == quant.MX_GROUP
+    # row-major exponent bytes read as little-endian int32 words: four groups per word
+    e = np.arange(8, dtype=np.uint8).reshape(1, 8) + 120
+    words = e.view("<u4")
+    assert words.shape == (1, 8 // c["ue8m0_values_per_int32"]["value"])
+    assert [(int(words[0, 1]) >> (8 * i)) & 0xFF for i in range(4)] == list(range(124, 128))
