@@ -2,39 +2,47 @@
 //
 // Operation (overview page, "Triton Fused MoE Kernel": every block of
 // BLOCK_SIZE_M sorted rows belongs to one expert; the quantized accumulation
-// is dequantised in float32 before the optional router-weight multiply;
-// "FusedMoE Class": w13 = gate+up and w2 = down, both [E, N, K]; fp8 oracle
-// API page: static 128x128 weight blocks, dynamic 128-group activations):
+// is dequantised in float32; "FusedMoE Class": w13 = gate+up and w2 = down,
+// both [E, N, K]; fp8 oracle API page: static 128x128 weight blocks,
+// dynamic 128-group activations, or the MXFP8 [1, 32] blocks):
 //
 //   GEMM1: h[r, n] = sum_kb xs[t, kb] * w13s[e, n/128, kb]
 //                      * sum_{k in kb} dec(xq[t, k]) * dec(w13[e, n, k])
 //          a = silu(h[:, :I]) * h[:, I:]  ->  per-row 128-group requant to
 //          (aq, as) in sorted order
-//   GEMM2: y[p, n] = w[p] * sum_kb as[r, kb] * w2s[e, n/128, kb]
+//   GEMM2: y[r, n] = sum_kb as[r, kb] * w2s[e, n/128, kb]
 //                      * sum_{k in kb} dec(aq[r, k]) * dec(w2[e, n, k])
+//          (bf16, sorted rows; the routing weight is the combine's)
 //
 // Common mapping onto gfx950.  A K step is one 128-wide scale block, so the
 // product of a block is a fresh MFMA result and its two scales are applied
 // once per output when it is folded into the accumulator: no partial sum
-// spans scale blocks.  Weights sit on the MFMA's M side (16 weight rows per
-// fragment) and tokens on its N side: decode-sized token counts still fill
-// an MFMA, and every lane ends up with four consecutive output features of
-// one token, which the epilogues store as packed words.  Each wave streams
-// its private weight rows from HBM straight into MFMA fragments one K block
-// ahead; the token tile of a K block is shared by the four waves of a
-// workgroup through an XOR-swizzled, double-buffered LDS tile.
+// spans scale blocks (with MXFP8 the MFMA applies the per-32 exponents and
+// the accumulator runs through it).  Weights sit on the MFMA's M side (16
+// weight rows per fragment) and tokens on its N side: decode-sized token
+// counts still fill an MFMA, and every lane ends up with four consecutive
+// output features of one token, which the epilogues store as packed words.
 //
-// GEMM2 uses v_mfma_f32_16x16x128_f8f6f4 (one per 16x16 tile and K block)
-// with a float32 accumulator; workgroup = BM sorted rows x 256 output
-// features, 64 per wave.  GEMM1 needs partial sums far more exact than the
-// FP8 MFMA gives (see moe_gemm1_kernel) and runs on f16 MFMAs of exactly
-// converted operands with float64 accumulation.
+// Two families:
+//   * decode (BM <= 64): each wave streams its private weight rows from HBM
+//     straight into MFMA fragments one K block ahead; the token tile of a K
+//     block is shared by the workgroup's waves through an XOR-swizzled,
+//     double-buffered LDS tile;
+//   * prefill (BM = 128): 128 rows x 256 weight rows per tile, 8 waves of
+//     64 x 64, operands staged through a three-stage LDS ring filled by
+//     direct global->LDS loads with hand-placed vmcnt waits; GEMM2 and the
+//     dense linears run persistent (one workgroup per CU).
+// GEMM2 uses v_mfma_f32_16x16x128_f8f6f4.  GEMM1 needs partial sums far
+// more exact than the FP8 MFMA gives (see moe_gemm1_kernel) and runs on f16
+// MFMAs of exactly converted operands, folded in float64 (decode) or float32
+// (prefill); the MXFP8 layer's GEMM1 runs on the scaled FP8 MFMA instead.
 //
-// Work order: logical tile L = m_block * n_tiles + n_tile, and the XCD
-// renumbering gives every XCD a contiguous range of L, so tiles sharing a
-// token tile or an expert's weight panel run on one XCD and meet in its L2.
-// Blocks past the padded row count (read on the device) leave at once, so the
-// grid is sized from the row capacity and the host never waits.
+// Work order: tiles are expert-major (the align scan publishes each expert's
+// first block), and the XCD renumbering gives every XCD a contiguous range,
+// so tiles sharing a token tile or an expert's weight panel run on one XCD
+// and meet in its L2.  Tiles past the padded row count (read on the device)
+// leave at once, so the grid is sized from the row capacity and the host
+// never waits.
 #include "device_common.hpp"
 #include "launch.hpp"
 

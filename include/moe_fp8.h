@@ -106,8 +106,8 @@ int moe_fp8_workspace_layout(int T, int H, int I, int E, int top_k,
  *   (xq, xs) = per-token 128-group FP8 quantisation of x
  *   h = block-scaled FP8 GEMM of xq with w13[e]        e = expert of the pair
  *   a = silu(h[:, :I]) * h[:, I:], requantised per token and 128-group
- *   y = block-scaled FP8 GEMM of a with w2[e], times the routing weight
- *   out[t] = bf16( sum over the top_k slots of y )
+ *   y = block-scaled FP8 GEMM of a with w2[e]
+ *   out[t] = bf16( sum over the top_k slots of w * y )
  *
  *   x             bf16    [T, H]
  *   router_logits float32 [T, E]
@@ -243,7 +243,7 @@ enum {
   MOE_STAGE_ALIGN,          /* sort and pad by expert (three kernels) */
   MOE_STAGE_QUANT,          /* activation quantisation of x */
   MOE_STAGE_GEMM1,          /* w13 GEMM + SiLU*mul + requantisation */
-  MOE_STAGE_GEMM2,          /* w2 GEMM + routing weight */
+  MOE_STAGE_GEMM2,          /* w2 GEMM (per sorted row, before the routing weight) */
   MOE_STAGE_COMBINE,        /* weighted sum over the top_k slots */
   MOE_STAGE_COUNT
 };
