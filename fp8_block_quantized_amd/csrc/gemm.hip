@@ -564,6 +564,7 @@ constexpr int kPf2S = 2048;                // token scales, eight 256-byte wave 
 
 struct TileId {
   int e, b, j, ks;
+  bool dead16;   // the 16 token rows this wave loads are all padding
 };
 
 // Logical tile L -> (expert, m block, n tile) in expert-major order, by a
@@ -589,8 +590,10 @@ __device__ __forceinline__ TileId tile_id(int L, const GemmArgs& a, int ksplit) 
   const int local = L - b0 * nt;
   const int grp = local / (kRowGroup * nt), rem = local - grp * kRowGroup * nt;
   const int left = nb - grp * kRowGroup, gb = left < kRowGroup ? left : kRowGroup;
-  const int j = rem / gb;
-  return {lo, b0 + grp * kRowGroup + (rem - j * gb), j, ks};
+  const int j = rem / gb, b = b0 + grp * kRowGroup + (rem - j * gb);
+  // padding rows are a suffix of the block: wave w loads token rows 16 w .. 16 w + 15
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return {lo, b, j, ks, load_uniform(a.sorted_ids + b * 128 + 16 * w) >= a.P};
 }
 
 template <bool kSplitK, bool kMx>
@@ -630,6 +633,9 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
   uint32_t aoff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) aoff[i] = (uint32_t)(((wave * 2 + i) * 8 + lr) * K + lc * 16);
+  // a slice of padding rows loads row 0 of the block instead (an L2 hit; the
+  // slots it fills feed only padding outputs)
+  const uint32_t aoff_dead = (uint32_t)(lc * 16);
   const uint32_t soff = (uint32_t)(((wave & 1) * 64 + lane) * nkb * 4);
   auto issue = [&](int stage, const TileId& t, const uint32_t (&wo)[4], int kb) {
     const uint32_t base = lds_offset(ring + stage * kStage);
@@ -640,7 +646,8 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16s(wo[i], wb, base + (wave * 4 + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16s(aoff[i], ab, base + kRingW + (wave * 2 + i) * 1024);
+    for (int i = 0; i < 2; ++i)
+      dma16s(t.dead16 ? aoff_dead : aoff[i], ab, base + kRingW + (wave * 2 + i) * 1024);
     if (kMx && wave >= 2 && wave < 6) {
       // exponent words of weight rows 256 j + 64 (wave - 2) + lane at K block kg
       const int row = 256 * t.j + 64 * (wave - 2) + lane;
