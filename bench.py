@@ -39,12 +39,12 @@ STAGE_PEAK = {"gemm1": MFMA_F16_PEAK, "gemm2": MFMA_FP8_PEAK}
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
 # kernel source they were taken on: bench reports null traffic once
 # gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "6707406ace4fdffe17133ddf3b09b04ec3fff86c55c35c0d8941244a405d562b"
+TRAFFIC_SOURCE_SHA256 = "959ecfd3d1c20a78a0f06ad3fdef8e679e170ef63b5d72c3300008eeac8906ba"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
-    "prefill.gemm1": (10750344255, 184535765),
-    "prefill.gemm2": (4419159031, 1207734795),
-    "decode.gemm1": (4795606118, 5720736),
-    "decode.gemm2": (2408613527, 7340363),
+    "prefill.gemm1": (10761369954, 184427744),
+    "prefill.gemm2": (4394785199, 1208380469),
+    "decode.gemm1": (4795570201, 5725131),
+    "decode.gemm2": (2408550955, 7340203),
 }
 
 
@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--phase", default="both", choices=["both", "decode", "prefill"],
                    help="time one batch size only (for per-kernel profiles)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--layer-only", action="store_true",
+                   help="time only the MoE layer (skip the standalone quantiser, dense linears, "
+                        "batched experts and MXFP8 layer)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run a plain device-to-device copy of this many MiB (three times), "
                         "the reference kernel that scales the HBM byte counters")
@@ -224,139 +227,148 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # standalone activation quantiser, rotating three input buffers (> MALL)
-    from synth import QUANT_WORKLOAD
-    M, K = QUANT_WORKLOAD["M"], QUANT_WORKLOAD["K"]
-    xq_in = [quant_input(device=dev, seed_base=4000 + 10 * i) for i in range(3)]
-    q_out = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(3)]
-    s_out = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(3)]
-    for i in range(3):
-        moe.per_token_group_quant_fp8(xq_in[i], q=q_out[i], scales=s_out[i])
-    qe = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        qe[2 * s].record()
-        moe.per_token_group_quant_fp8(xq_in[s % 3], q=q_out[s % 3], scales=s_out[s % 3])
-        qe[2 * s + 1].record()
-    torch.cuda.synchronize()
-    q_ms = float(np.mean([qe[2 * s].elapsed_time(qe[2 * s + 1]) for s in range(args.steps)]))
-    q_bytes = 2 * M * K + M * K + 4 * M * (K // 128)
-    quant = {"M": M, "K": K, "ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
-             "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
+    def extras():
+        """The timed sections after the layer: standalone quantiser, dense
+        linears, batched experts and the MXFP8 layer."""
+        # standalone activation quantiser, rotating three input buffers (> MALL)
+        from synth import QUANT_WORKLOAD
+        M, K = QUANT_WORKLOAD["M"], QUANT_WORKLOAD["K"]
+        xq_in = [quant_input(device=dev, seed_base=4000 + 10 * i) for i in range(3)]
+        q_out = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(3)]
+        s_out = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(3)]
+        for i in range(3):
+            moe.per_token_group_quant_fp8(xq_in[i], q=q_out[i], scales=s_out[i])
+        qe = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            qe[2 * s].record()
+            moe.per_token_group_quant_fp8(xq_in[s % 3], q=q_out[s % 3], scales=s_out[s % 3])
+            qe[2 * s + 1].record()
+        torch.cuda.synchronize()
+        q_ms = float(np.mean([qe[2 * s].elapsed_time(qe[2 * s + 1]) for s in range(args.steps)]))
+        q_bytes = 2 * M * K + M * K + 4 * M * (K // 128)
+        quant = {"M": M, "K": K, "ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
+                 "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
 
-    # the same quantiser with MXFP8 scales: groups of 32, UE8M0 exponent bytes
-    e_out = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(3)]
-    for i in range(3):
-        moe.per_token_group_quant_fp8_fmt(xq_in[i], 32, "ue8m0", q=q_out[i], scales=e_out[i])
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        qe[2 * s].record()
-        moe.per_token_group_quant_fp8_fmt(xq_in[s % 3], 32, "ue8m0", q=q_out[s % 3], scales=e_out[s % 3])
-        qe[2 * s + 1].record()
-    torch.cuda.synchronize()
-    q_ms = float(np.mean([qe[2 * s].elapsed_time(qe[2 * s + 1]) for s in range(args.steps)]))
-    q_bytes = 2 * M * K + M * K + M * (K // 32)
-    quant["mxfp8_group32_ue8m0"] = {"ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
-                                    "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
-    del xq_in, q_out, s_out, e_out
+        # the same quantiser with MXFP8 scales: groups of 32, UE8M0 exponent bytes
+        e_out = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(3)]
+        for i in range(3):
+            moe.per_token_group_quant_fp8_fmt(xq_in[i], 32, "ue8m0", q=q_out[i], scales=e_out[i])
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            qe[2 * s].record()
+            moe.per_token_group_quant_fp8_fmt(xq_in[s % 3], 32, "ue8m0", q=q_out[s % 3], scales=e_out[s % 3])
+            qe[2 * s + 1].record()
+        torch.cuda.synchronize()
+        q_ms = float(np.mean([qe[2 * s].elapsed_time(qe[2 * s + 1]) for s in range(args.steps)]))
+        q_bytes = 2 * M * K + M * K + M * (K // 32)
+        quant["mxfp8_group32_ue8m0"] = {"ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
+                                        "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
+        del xq_in, q_out, s_out, e_out
 
-    # dense linears (the layer's E = 1 neighbour), decode and prefill batches:
-    # block FP8 (128x128 weight blocks, float32 scales) and MXFP8 ([1, 32], UE8M0)
-    from synth import LINEAR_WORKLOAD, MX_LINEAR_WORKLOAD, make_linear, make_mx_linear
+        # dense linears (the layer's E = 1 neighbour), decode and prefill batches:
+        # block FP8 (128x128 weight blocks, float32 scales) and MXFP8 ([1, 32], UE8M0)
+        from synth import LINEAR_WORKLOAD, MX_LINEAR_WORKLOAD, make_linear, make_mx_linear
 
-    def time_linear(fn, ws_bytes, make, wl, scale_bytes):
-        LN, LK = wl["N"], wl["K"]
-        res = {"workload": f"DeepSeek-V3-shaped dense down projection N={LN} K={LK}"}
-        for LM in wl["M"]:
-            lx, lw, lws = make(LM, LN, LK, 1000 * wl["index"], device=dev)
-            lout = torch.empty((LM, LN), dtype=torch.bfloat16, device=dev)
-            lwsp = torch.empty(ws_bytes(LM, LN, LK), dtype=torch.uint8, device=dev)
-            for _ in range(3):
-                fn(lx, lw, lws, out=lout, workspace=lwsp)
-            le = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            torch.cuda.synchronize()
-            le[0].record()
-            for _ in range(args.steps):
-                fn(lx, lw, lws, out=lout, workspace=lwsp)
-            le[1].record()
-            torch.cuda.synchronize()
-            lms = le[0].elapsed_time(le[1]) / args.steps
-            lbytes = LN * LK + scale_bytes(LN, LK) + 2 * LM * LK + 2 * LM * LN
-            r = roofline_of(lbytes, 2 * LM * LN * LK, lms * 1e-3, MFMA_FP8_PEAK)
-            r.update({"M": LM, "ms": lms, "alg_bytes": lbytes, "alg_flops": 2 * LM * LN * LK})
-            res[f"M{LM}"] = r
-            del lx, lw, lws, lout, lwsp
-        return res
+        def time_linear(fn, ws_bytes, make, wl, scale_bytes):
+            LN, LK = wl["N"], wl["K"]
+            res = {"workload": f"DeepSeek-V3-shaped dense down projection N={LN} K={LK}"}
+            for LM in wl["M"]:
+                lx, lw, lws = make(LM, LN, LK, 1000 * wl["index"], device=dev)
+                lout = torch.empty((LM, LN), dtype=torch.bfloat16, device=dev)
+                lwsp = torch.empty(ws_bytes(LM, LN, LK), dtype=torch.uint8, device=dev)
+                for _ in range(3):
+                    fn(lx, lw, lws, out=lout, workspace=lwsp)
+                le = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                torch.cuda.synchronize()
+                le[0].record()
+                for _ in range(args.steps):
+                    fn(lx, lw, lws, out=lout, workspace=lwsp)
+                le[1].record()
+                torch.cuda.synchronize()
+                lms = le[0].elapsed_time(le[1]) / args.steps
+                lbytes = LN * LK + scale_bytes(LN, LK) + 2 * LM * LK + 2 * LM * LN
+                r = roofline_of(lbytes, 2 * LM * LN * LK, lms * 1e-3, MFMA_FP8_PEAK)
+                r.update({"M": LM, "ms": lms, "alg_bytes": lbytes, "alg_flops": 2 * LM * LN * LK})
+                res[f"M{LM}"] = r
+                del lx, lw, lws, lout, lwsp
+            return res
 
-    dense = time_linear(moe.fp8_block_linear, moe.fp8_block_linear_workspace_bytes, make_linear,
-                        LINEAR_WORKLOAD, lambda n, k: 4 * (n // 128) * (k // 128))
-    dense_mx = time_linear(moe.mxfp8_linear, moe.mxfp8_linear_workspace_bytes, make_mx_linear,
-                           MX_LINEAR_WORKLOAD, lambda n, k: n * (k // 32))
+        dense = time_linear(moe.fp8_block_linear, moe.fp8_block_linear_workspace_bytes, make_linear,
+                            LINEAR_WORKLOAD, lambda n, k: 4 * (n // 128) * (k // 128))
+        dense_mx = time_linear(moe.mxfp8_linear, moe.mxfp8_linear_workspace_bytes, make_mx_linear,
+                               MX_LINEAR_WORKLOAD, lambda n, k: n * (k // 32))
 
-    # batched (masked) expert format: one rank's experts, device-side counts
-    from synth import BATCHED_WORKLOAD as BW
-    bE, bM, bH, bI = BW["E"], BW["M"], BW["H"], BW["I"]
-    gb = torch.Generator(device="cpu").manual_seed(1000 * BW["index"] + 1)
-    bcounts = torch.randint(BW["min_count"], bM + 1, (bE,), generator=gb, dtype=torch.int32)
-    bx = torch.randn((bE, bM, bH), generator=torch.Generator(device=dev).manual_seed(1000 * BW["index"]),
-                     device=dev).to(torch.bfloat16)
-    bw = make_weights(bH, bI, bE, 1000 * BW["index"] + 2, dev)
-    bc_dev = bcounts.to(dev)
-    bout = torch.empty_like(bx)
-    bws = torch.empty(moe.moe_fp8_batched_workspace_bytes(bE, bM, bH, bI), dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws)
-    be = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    be[0].record()
-    for _ in range(args.steps):
-        moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws)
-    be[1].record()
-    torch.cuda.synchronize()
-    bms = be[0].elapsed_time(be[1]) / args.steps
-    rows = int(bcounts.sum())
-    active = int((bcounts > 0).sum())
-    wbytes = active * (2 * bI * bH + bH * bI + 4 * (2 * bI // 128) * (bH // 128) + 4 * (bH // 128) * (bI // 128))
-    bbytes = wbytes + 2 * rows * bH + 2 * bE * bM * bH
-    bflops = 6 * rows * bH * bI
-    # GEMM1 (4 H I flops per row) runs on f16 MFMAs, GEMM2 (2 H I) on FP8 ones:
-    # the peak of the mix is 6 / (4 / f16 peak + 2 / FP8 peak)
-    blend = 6.0 / (4.0 / MFMA_F16_PEAK + 2.0 / MFMA_FP8_PEAK)
-    batched = roofline_of(bbytes, bflops, bms * 1e-3, blend)
-    batched.update({"workload": f"DeepSeek-V3-shaped experts of one rank of eight: E={bE} max_tokens={bM} "
-                                f"H={bH} I={bI}, counts uniform in [{BW['min_count']}, {bM}]",
-                    "rows": rows, "ms": bms, "alg_bytes": bbytes, "alg_flops": bflops})
-    del bx, bw, bout, bws
-
-    # the MXFP8 layer ([1, 32] blocks, UE8M0 scales, FP8 MFMAs in both GEMMs)
-    # on the same inputs, with the same weights cast to MXFP8
-    from synth import make_mx_weights
-    mxw = make_mx_weights(H, I, E, base + 2, dev)
-    mx_layer = {"workload": f"{args.workload}-shaped MoE layer with MXFP8 weights and activations"}
-    for n in order:
-        ph = phases[n]
-        T = ph["T"]
-        mws = torch.empty(moe.moe_fp8_mx_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
+        # batched (masked) expert format: one rank's experts, device-side counts
+        from synth import BATCHED_WORKLOAD as BW
+        bE, bM, bH, bI = BW["E"], BW["M"], BW["H"], BW["I"]
+        gb = torch.Generator(device="cpu").manual_seed(1000 * BW["index"] + 1)
+        bcounts = torch.randint(BW["min_count"], bM + 1, (bE,), generator=gb, dtype=torch.int32)
+        bx = torch.randn((bE, bM, bH), generator=torch.Generator(device=dev).manual_seed(1000 * BW["index"]),
+                         device=dev).to(torch.bfloat16)
+        bw = make_weights(bH, bI, bE, 1000 * BW["index"] + 2, dev)
+        bc_dev = bcounts.to(dev)
+        bout = torch.empty_like(bx)
+        bws = torch.empty(moe.moe_fp8_batched_workspace_bytes(bE, bM, bH, bI), dtype=torch.uint8, device=dev)
         for _ in range(3):
-            moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True, out=ph["out"], workspace=mws)
-        me = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws)
+        be = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
-        me[0].record()
+        be[0].record()
         for _ in range(args.steps):
-            moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True, out=ph["out"], workspace=mws)
-        me[1].record()
+            moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws)
+        be[1].record()
         torch.cuda.synchronize()
-        mms = me[0].elapsed_time(me[1]) / args.steps
-        ids = moe.workspace_taps(mws, T, H, I, E, k, mx=True)["topk_ids"].cpu().numpy()
-        e_act = int(np.unique(ids).size)
-        mbytes = e_act * (2 * I * H + H * I) * 33 // 32 + 4 * T * H
-        mflops = 6 * T * k * H * I
-        r = roofline_of(mbytes, mflops, mms * 1e-3, MFMA_FP8_PEAK)
-        r.update({"T": T, "ms": mms, "tokens_per_s": T / (mms * 1e-3), "active_experts": e_act,
-                  "alg_bytes": mbytes, "alg_flops": mflops})
-        mx_layer[n] = r
-        del mws
-    del mxw
+        bms = be[0].elapsed_time(be[1]) / args.steps
+        rows = int(bcounts.sum())
+        active = int((bcounts > 0).sum())
+        wbytes = active * (2 * bI * bH + bH * bI + 4 * (2 * bI // 128) * (bH // 128) + 4 * (bH // 128) * (bI // 128))
+        bbytes = wbytes + 2 * rows * bH + 2 * bE * bM * bH
+        bflops = 6 * rows * bH * bI
+        # GEMM1 (4 H I flops per row) runs on f16 MFMAs, GEMM2 (2 H I) on FP8 ones:
+        # the peak of the mix is 6 / (4 / f16 peak + 2 / FP8 peak)
+        blend = 6.0 / (4.0 / MFMA_F16_PEAK + 2.0 / MFMA_FP8_PEAK)
+        batched = roofline_of(bbytes, bflops, bms * 1e-3, blend)
+        batched.update({"workload": f"DeepSeek-V3-shaped experts of one rank of eight: E={bE} max_tokens={bM} "
+                                    f"H={bH} I={bI}, counts uniform in [{BW['min_count']}, {bM}]",
+                        "rows": rows, "ms": bms, "alg_bytes": bbytes, "alg_flops": bflops})
+        del bx, bw, bout, bws
+
+        # the MXFP8 layer ([1, 32] blocks, UE8M0 scales, FP8 MFMAs in both GEMMs)
+        # on the same inputs, with the same weights cast to MXFP8
+        from synth import make_mx_weights
+        mxw = make_mx_weights(H, I, E, base + 2, dev)
+        mx_layer = {"workload": f"{args.workload}-shaped MoE layer with MXFP8 weights and activations"}
+        for n in order:
+            ph = phases[n]
+            T = ph["T"]
+            mws = torch.empty(moe.moe_fp8_mx_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True, out=ph["out"], workspace=mws)
+            me = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            me[0].record()
+            for _ in range(args.steps):
+                moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True, out=ph["out"], workspace=mws)
+            me[1].record()
+            torch.cuda.synchronize()
+            mms = me[0].elapsed_time(me[1]) / args.steps
+            ids = moe.workspace_taps(mws, T, H, I, E, k, mx=True)["topk_ids"].cpu().numpy()
+            e_act = int(np.unique(ids).size)
+            mbytes = e_act * (2 * I * H + H * I) * 33 // 32 + 4 * T * H
+            mflops = 6 * T * k * H * I
+            r = roofline_of(mbytes, mflops, mms * 1e-3, MFMA_FP8_PEAK)
+            r.update({"T": T, "ms": mms, "tokens_per_s": T / (mms * 1e-3), "active_experts": e_act,
+                      "alg_bytes": mbytes, "alg_flops": mflops})
+            mx_layer[n] = r
+            del mws
+        del mxw
+        return quant, dense, dense_mx, batched, mx_layer
+
+    if args.layer_only:
+        quant = dense = dense_mx = batched = mx_layer = None
+    else:
+        quant, dense, dense_mx, batched, mx_layer = extras()
 
     dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
     dom = kernels[dom_name]
