@@ -206,9 +206,9 @@ def moe_fp8_forward_routed(x, router_logits, w13, w13_scale, w2, w2_scale, top_k
 
 def workspace_taps(workspace, T, H, I, E, top_k, mx=False):
     """Views of the forward's intermediates inside its workspace (mx: the
-    MXFP8 layer's, block_m 128 and exponent bytes in xs / as)."""
+    MXFP8 layer's, with exponent bytes in xs / as)."""
     off = moe_fp8_workspace_layout(T, H, I, E, top_k, mx)
-    bm = 128 if mx else moe_fp8_block_m(T, H, I, E, top_k)
+    bm = moe_fp8_block_m(T, H, I, E, top_k)
     P = T * top_k
     cap = -(-(P + E * (bm - 1)) // bm) * bm
 

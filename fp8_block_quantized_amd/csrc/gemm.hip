@@ -152,7 +152,9 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
   return r;
 }
 
-template <int BM>
+// kMx: MXFP8 operands (exponent bytes per row and 32 K elements, applied by
+// the MFMA itself; the accumulator runs through it with no fold)
+template <int BM, bool kMx = false>
 __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   constexpr int NQ = BM / 16;                  // token sub-tiles
   constexpr int CHUNKS = BM * 8;               // 16-byte chunks of a token tile
@@ -180,7 +182,14 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   for (int pp = 0; pp < 4; ++pp)
     wptr[pp] = wbase + (size_t)(wave_on ? prow[pp] + l16 : l16) * K + g * 16;
   const int nblk_n = args.N >> 7;
-  const float* ws0 = args.w_scale + ((size_t)e * nblk_n + (wave_on ? (256 * j + 64 * wave) >> 7 : 0)) * nkb;
+  const float* ws0 = kMx ? nullptr
+                         : args.w_scale + ((size_t)e * nblk_n + (wave_on ? (256 * j + 64 * wave) >> 7 : 0)) * nkb;
+  // MX: this lane's exponent byte of each fragment row, block g of K block kb at + 4 kb
+  const uint8_t* wep[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+    wep[pp] = (const uint8_t*)args.w_scale +
+              ((size_t)e * args.N + (wave_on ? prow[pp] + l16 : l16)) * (nkb * 4) + g;
 
   // ---- token side: BM x 128 tile per K block, staged in LDS ----
   const uint8_t* aptr[CPT];
@@ -197,11 +206,13 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
     }
   }
   const float* sptr[NQ];
+  const uint8_t* aep[NQ];
   int qoff0[NQ], qoff1[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int rq = 16 * q + l16;
     sptr[q] = args.act_scale + (size_t)(row0 + rq) * nkb;
+    aep[q] = (const uint8_t*)args.act_scale + (size_t)(row0 + rq) * (nkb * 4) + g;
     qoff0[q] = rq * 128 + ((g ^ (rq & 7)) << 4);
     qoff1[q] = rq * 128 + (((g + 4) ^ (rq & 7)) << 4);
   }
@@ -214,9 +225,16 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) wcur[pp] = load_frag_global(wptr[pp]);
   float sa[NQ];
+  int ew[4], ea[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) sa[q] = sptr[q][0];
-  float sw0 = ws0[0];
+  for (int q = 0; q < NQ; ++q) {
+    if (kMx) ea[q] = aep[q][0];
+    else sa[q] = sptr[q][0];
+  }
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+    if (kMx) ew[pp] = wep[pp][0];
+  float sw0 = kMx ? 0.0f : ws0[0];
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
     if (soff[i] >= 0) *(uint4*)(&smem[0][soff[i]]) = areg[i];
@@ -241,9 +259,16 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) wnext[pp] = load_frag_global(wptr[pp] + koff);
     float sa_n[NQ];
+    int ew_n[4], ea_n[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) sa_n[q] = sptr[q][kn];
-    const float sw0_n = ws0[kn];
+    for (int q = 0; q < NQ; ++q) {
+      if (kMx) ea_n[q] = aep[q][4 * kn];
+      else sa_n[q] = sptr[q][kn];
+    }
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+      if (kMx) ew_n[pp] = wep[pp][4 * kn];
+    const float sw0_n = kMx ? 0.0f : ws0[kn];
 
     // MFMAs on K block kb
 #pragma unroll
@@ -253,13 +278,20 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
       v8i bq;
       bq[0] = t0.x; bq[1] = t0.y; bq[2] = t0.z; bq[3] = t0.w;
       bq[4] = t1.x; bq[5] = t1.y; bq[6] = t1.z; bq[7] = t1.w;
-      const float sc = sa[q] * sw0;
+      if (kMx) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            wcur[pp], bq, zero, 0, 0, 0, 0, 0, 0);
+        for (int pp = 0; pp < 4; ++pp)
+          acc[pp][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[pp], bq, acc[pp][q], 0, 0,
+                                                                       0, ew[pp], 0, ea[q]);
+      } else {
+        const float sc = sa[q] * sw0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
+        for (int pp = 0; pp < 4; ++pp) {
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wcur[pp], bq, zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
+        }
       }
     }
     if (kb + 1 < nkb) {
@@ -269,9 +301,15 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
     }
     __syncthreads();
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) wcur[pp] = wnext[pp];
+    for (int pp = 0; pp < 4; ++pp) {
+      wcur[pp] = wnext[pp];
+      if (kMx) ew[pp] = ew_n[pp];
+    }
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) sa[q] = sa_n[q];
+    for (int q = 0; q < NQ; ++q) {
+      if (kMx) ea[q] = ea_n[q];
+      else sa[q] = sa_n[q];
+    }
     sw0 = sw0_n;
   }
 
@@ -1102,10 +1140,165 @@ __global__ __launch_bounds__(512) void moe_gemm1_mx_kernel(GemmArgs args) {
   }
 }
 
+// GEMM1 of the MXFP8 layer at decode sizes (block_m <= 64): the structure of
+// moe_gemm2_kernel (each wave streams its weight rows from HBM into MFMA
+// fragments one K block ahead; the e4m3 token rows, gathered through the
+// sorted layout, are shared through a double-buffered LDS tile), the
+// exponent bytes loaded with their operands and applied by the MFMA, and
+// moe_gemm1_mx_kernel's epilogue: wave w holds the gate and up rows of
+// features 32 w .. 32 w + 31 of the tile's 128, one requant group.
+template <int RM>
+__global__ __launch_bounds__(256) void moe_gemm1_mx_dec_kernel(GemmArgs args, int BM) {
+  constexpr int NQ = RM / 16;
+  constexpr int CHUNKS = RM * 8;               // 16-byte chunks of a token tile
+  constexpr int CPT = (CHUNKS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][RM * 128];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const TileCoord tc = tile_of(blockIdx.x, args);
+  if (!tc.valid) return;
+  const int b = tc.b, half = tc.half, j = tc.j;
+  const int row0 = b * BM + half * RM;
+  if (load_uniform(args.sorted_ids + row0) >= args.P) return;   // padding only
+  const int e = load_uniform(args.expert_ids + b);
+  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * j;
+
+  const uint8_t* wptr[4];
+  const uint8_t* wep[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int row = (pp < 2 ? 0 : I) + i0 + 32 * wave + 16 * (pp & 1) + l16;
+    wptr[pp] = args.w + ((size_t)e * args.N + row) * K + g * 16;
+    wep[pp] = (const uint8_t*)args.w_scale + ((size_t)e * args.N + row) * (nkb * 4) + g;
+  }
+  const uint8_t* aptr[CPT];
+  int soff[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i;
+    aptr[i] = nullptr;
+    soff[i] = -1;
+    if (c < CHUNKS) {
+      const int r = c >> 3, ch = c & 7;
+      soff[i] = r * 128 + ((ch ^ (r & 7)) << 4);
+      const int p = args.sorted_ids[row0 + r];
+      if (p < args.P) aptr[i] = args.act + (size_t)(p / args.top_k) * K + ch * 16;
+    }
+  }
+  const uint8_t* aep[NQ];
+  int qoff0[NQ], qoff1[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int rq = 16 * q + l16;
+    const int p = args.sorted_ids[row0 + rq];
+    aep[q] = p < args.P ? (const uint8_t*)args.act_scale + (size_t)(p / args.top_k) * (nkb * 4) + g
+                        : nullptr;
+    qoff0[q] = rq * 128 + ((g ^ (rq & 7)) << 4);
+    qoff1[q] = rq * 128 + (((g + 4) ^ (rq & 7)) << 4);
+  }
+
+  uint4 areg[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) areg[i] = aptr[i] ? *(const uint4*)aptr[i] : make_uint4(0, 0, 0, 0);
+  v8i wcur[4];
+  int ew[4], ea[NQ];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    wcur[pp] = load_frag_global(wptr[pp]);
+    ew[pp] = wep[pp][0];
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) ea[q] = aep[q] ? aep[q][0] : 127;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+    if (soff[i] >= 0) *(uint4*)(&smem[0][soff[i]]) = areg[i];
+  __syncthreads();
+
+  v4f acc[4][NQ];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    const int kn = kb + 1 < nkb ? kb + 1 : kb;     // the last prefetch re-reads
+    const size_t koff = (size_t)kn * 128;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      areg[i] = aptr[i] ? *(const uint4*)(aptr[i] + koff) : make_uint4(0, 0, 0, 0);
+    v8i wnext[4];
+    int ew_n[4], ea_n[NQ];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      wnext[pp] = load_frag_global(wptr[pp] + koff);
+      ew_n[pp] = wep[pp][4 * kn];
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) ea_n[q] = aep[q] ? aep[q][4 * kn] : 127;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const uint4 t0 = *(const uint4*)(&smem[buf][qoff0[q]]);
+      const uint4 t1 = *(const uint4*)(&smem[buf][qoff1[q]]);
+      v8i bq;
+      bq[0] = t0.x; bq[1] = t0.y; bq[2] = t0.z; bq[3] = t0.w;
+      bq[4] = t1.x; bq[5] = t1.y; bq[6] = t1.z; bq[7] = t1.w;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp)
+        acc[pp][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[pp], bq, acc[pp][q], 0, 0, 0,
+                                                                     ew[pp], 0, ea[q]);
+    }
+    if (kb + 1 < nkb) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (soff[i] >= 0) *(uint4*)(&smem[buf ^ 1][soff[i]]) = areg[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      wcur[pp] = wnext[pp];
+      ew[pp] = ew_n[pp];
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) ea[q] = ea_n[q];
+  }
+
+  // a = silu(gate) * up, requantised per token row and 32-feature group;
+  // padding rows are not written (nothing reads them)
+  uint8_t* ae = (uint8_t*)args.as_out;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    float av[2][4];
+    float m = 0.0f;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gt = acc[pg][q][r], up = acc[pg + 2][q][r];
+        av[pg][r] = gt / (1.0f + expf(-gt)) * up;
+        m = __builtin_fmaxf(m, __builtin_fabsf(av[pg][r]));
+      }
+    m = __builtin_fmaxf(m, __shfl_xor(m, 16));
+    m = __builtin_fmaxf(m, __shfl_xor(m, 32));
+    const uint32_t sb = ceil_pow2_bits(__builtin_fmaxf(m, kAmaxEps) / kFp8Max);
+    const float rcp = __uint_as_float((254u - (sb >> 23)) << 23);
+    const int grow = row0 + 16 * q + l16;
+    if (args.sorted_ids[grow] >= args.P) continue;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const uint32_t word = pack4_e4m3(clamp_fp8(av[pg][0] * rcp), clamp_fp8(av[pg][1] * rcp),
+                                       clamp_fp8(av[pg][2] * rcp), clamp_fp8(av[pg][3] * rcp));
+      *(uint32_t*)(args.aq_out + (size_t)grow * I + i0 + 32 * wave + 16 * pg + 4 * g) = word;
+    }
+    if (g == 0) ae[(size_t)grow * (I >> 5) + ((i0 + 32 * wave) >> 5)] = (uint8_t)(sb >> 23);
+  }
+}
+
 hipError_t launch_gemm1_mx(const uint8_t* xq, const uint8_t* xe, const uint8_t* w13,
                            const uint8_t* w13e, const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const int32_t* eoff, int E, int H, int I, int P,
-                           int top_k, int nblk, uint8_t* aq, uint8_t* ae, hipStream_t stream) {
+                           int top_k, int BM, int nblk, uint8_t* aq, uint8_t* ae, hipStream_t stream) {
   GemmArgs a{};
   a.eoff = eoff; a.E = E; a.split = 1;
   a.act = xq; a.act_scale = (const float*)xe; a.w = w13; a.w_scale = (const float*)w13e;
@@ -1113,7 +1306,19 @@ hipError_t launch_gemm1_mx(const uint8_t* xq, const uint8_t* xe, const uint8_t* 
   a.aq_out = aq; a.as_out = (float*)ae;
   a.K = H; a.N = 2 * I; a.I = I; a.H = H; a.P = P; a.top_k = top_k;
   a.nblk = nblk; a.n_tiles = I / 128; a.mx = 1;
-  hipLaunchKernelGGL(moe_gemm1_mx_kernel, dim3((unsigned)(nblk * a.n_tiles)), dim3(512), 0, stream, a);
+  if (BM == 128) {
+    hipLaunchKernelGGL(moe_gemm1_mx_kernel, dim3((unsigned)(nblk * a.n_tiles)), dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int rm = BM < 32 ? BM : 32;
+  a.split = BM / rm;
+  const dim3 grid((unsigned)(nblk * a.split * a.n_tiles)), block(256);
+  if (rm == 16)
+    hipLaunchKernelGGL(moe_gemm1_mx_dec_kernel<16>, grid, block, 0, stream, a, BM);
+  else if (rm == 32)
+    hipLaunchKernelGGL(moe_gemm1_mx_dec_kernel<32>, grid, block, 0, stream, a, BM);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -1150,7 +1355,15 @@ static hipError_t launch_reduce_slices(const float* part, int ksplit, int rows, 
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
   const bool persistent = BM == 128 && (a.K >> 7) / a.ksplit >= 2;
-  if (a.mx && !persistent) return hipErrorInvalidValue;     // exponent scales: persistent kernel only
+  if (a.mx && !persistent) {       // exponent scales: the persistent kernel, or the decode ones
+    switch (BM) {
+      case 16: hipLaunchKernelGGL((moe_gemm2_kernel<16, true>), grid, block, 0, stream, a); break;
+      case 32: hipLaunchKernelGGL((moe_gemm2_kernel<32, true>), grid, block, 0, stream, a); break;
+      case 64: hipLaunchKernelGGL((moe_gemm2_kernel<64, true>), grid, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (persistent) {
     // one persistent workgroup per CU, a multiple of the 8 XCDs
     int dev = 0, cus = 0;
@@ -1228,17 +1441,17 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
 
 hipError_t launch_gemm2_mx(const uint8_t* aq, const uint8_t* ae, const uint8_t* w2, const uint8_t* w2e,
                            const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
-                           const int32_t* eoff, int E, int H, int I, int P, int nblk, uint16_t* y,
-                           int y_stride, hipStream_t stream) {
+                           const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
+                           uint16_t* y, int y_stride, hipStream_t stream) {
   GemmArgs a{};
   a.eoff = eoff; a.E = E; a.split = 1; a.mx = 1;
   a.act = aq; a.act_scale = (const float*)ae; a.w = w2; a.w_scale = (const float*)w2e;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
   a.y_out = y; a.y_stride = y_stride;
-  a.y_rows = nblk * 128; a.y_cols = y_stride; a.y_dump = y; a.ksplit = 1;
+  a.y_rows = nblk * BM; a.y_cols = y_stride; a.y_dump = y; a.ksplit = 1;
   a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
   a.n_tiles = (H + 255) / 256; a.nblk = nblk;
-  return launch_gemm2_bm(a, 128, stream);
+  return launch_gemm2_bm(a, BM, stream);
 }
 
 hipError_t launch_gemm2_bounded(const uint8_t* act, const float* act_scale, const uint8_t* w,

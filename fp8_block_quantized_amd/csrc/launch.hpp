@@ -36,17 +36,17 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
                         uint16_t* y, int y_stride, hipStream_t stream);
-// The MXFP8 layer's GEMMs (block_m 128): exponent bytes [rows, K/32] for the
-// activations, [E, N, K/32] for the weights; GEMM1 writes the requantised
-// activation's exponent bytes [cap, I/32] into ae
+// The MXFP8 layer's GEMMs (block_m 16 to 128): exponent bytes [rows, K/32]
+// for the activations, [E, N, K/32] for the weights; GEMM1 writes the
+// requantised activation's exponent bytes [cap, I/32] into ae
 hipError_t launch_gemm1_mx(const uint8_t* xq, const uint8_t* xe, const uint8_t* w13,
                            const uint8_t* w13e, const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const int32_t* eoff, int E, int H, int I, int P,
-                           int top_k, int nblk, uint8_t* aq, uint8_t* ae, hipStream_t stream);
+                           int top_k, int BM, int nblk, uint8_t* aq, uint8_t* ae, hipStream_t stream);
 hipError_t launch_gemm2_mx(const uint8_t* aq, const uint8_t* ae, const uint8_t* w2, const uint8_t* w2e,
                            const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
-                           const int32_t* eoff, int E, int H, int I, int P, int nblk, uint16_t* y,
-                           int y_stride, hipStream_t stream);
+                           const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
+                           uint16_t* y, int y_stride, hipStream_t stream);
 // GEMM2 with an output bounded to rows [0, y_rows) and columns [0, y_cols):
 // stores outside go to a 1024-byte dump; with ksplit > 1, K slices go to
 // float32 partials [ksplit, y_rows, y_cols] and are summed into y (the dense linear).

@@ -370,7 +370,7 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, con
 size_t moe_fp8_mx_workspace_bytes(int T, int H, int I, int E, int top_k) {
   if (check_moe_shape(T, H, I, E, top_k) != MOE_OK || I < 256) return 0;
   Layout L;
-  make_layout(T, H, I, E, top_k, L, 128);
+  make_layout(T, H, I, E, top_k, L);
   return L.total;
 }
 
@@ -381,7 +381,7 @@ int moe_fp8_mx_workspace_layout(int T, int H, int I, int E, int top_k,
   if (st != MOE_OK) return st;
   if (I < 256) return MOE_ERR_UNSUPPORTED;
   Layout L;
-  make_layout(T, H, I, E, top_k, L, 128);
+  make_layout(T, H, I, E, top_k, L);
   for (int i = 0; i < MOE_TAP_COUNT; ++i) offsets[i] = L.off[i];
   return MOE_OK;
 }
@@ -397,7 +397,7 @@ int moe_fp8_mx_forward(const void* x, const float* router_logits, const uint8_t*
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_SHAPE;
   if (I < 256) return MOE_ERR_UNSUPPORTED;
   Layout L;
-  make_layout(T, H, I, E, top_k, L, 128);
+  make_layout(T, H, I, E, top_k, L);
   if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_ERR_WORKSPACE;
   if ((uintptr_t)x % 16 || (uintptr_t)out % 16 || (uintptr_t)w13 % 16 || (uintptr_t)w2 % 16 ||
       (uintptr_t)router_logits % 4 || (uintptr_t)w13_scale % 4 || (uintptr_t)w2_scale % 4)
@@ -432,10 +432,10 @@ int moe_fp8_mx_forward(const void* x, const float* router_logits, const uint8_t*
     return MOE_ERR_HIP;
   if (moe::launch_group_quant_fmt(x, T, H, 32, moe::kScaleUe8m0, xq, xe, stream)) return MOE_ERR_HIP;
   const int32_t* eoff = moe::align_expert_offsets(scratch, P, E);
-  if (moe::launch_gemm1_mx(xq, xe, w13, w13_scale, sorted, eids, ntpp, eoff, E, H, I, P, top_k, nblk,
-                           aq, ae, stream))
+  if (moe::launch_gemm1_mx(xq, xe, w13, w13_scale, sorted, eids, ntpp, eoff, E, H, I, P, top_k,
+                           L.BM, nblk, aq, ae, stream))
     return MOE_ERR_HIP;
-  if (moe::launch_gemm2_mx(aq, ae, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, P, nblk, y,
+  if (moe::launch_gemm2_mx(aq, ae, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, P, L.BM, nblk, y,
                            (int)y_stride(H), stream))
     return MOE_ERR_HIP;
   if (moe::launch_combine(y, (int)y_stride(H), ppos, tw, T, H, top_k, (uint16_t*)out, stream))

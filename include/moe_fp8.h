@@ -212,7 +212,7 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens,
  *   y = the same block-scaled product of a with w2[e]
  *   out[t] = bf16( sum over the top_k slots of w * y )
  * Both GEMMs run on FP8 MFMAs that apply the exponents in hardware
- * (float32 accumulation), the block size is always 128.
+ * (float32 accumulation); the block size is moe_fp8_block_m()'s.
  *
  *   x             bf16    [T, H]
  *   router_logits float32 [T, E]

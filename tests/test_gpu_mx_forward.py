@@ -2,7 +2,7 @@
 against the oracle (oracle/moe.py, moe_forward with mx=True).
 
 Exact targets, read from the workspace taps: routing ids, the sort-and-pad
-layout (block 128) and the group-32 activation codes and UE8M0 bytes of x.
+layout and the group-32 activation codes and UE8M0 bytes of x.
 The requantised activation is not an exact target: both GEMMs accumulate on
 FP8 MFMAs that apply the exponents in hardware (about 1e-6 of sum |p| on
 operands of normal magnitude), so an element next to a rounding midpoint,
@@ -66,8 +66,9 @@ def _run(x, logits, w, T, H, I, E, k):
 def _check_front(taps, x_np, rids, rw, E):
     assert np.array_equal(np_(taps["topk_ids"]), rids), "ids"
     np.testing.assert_allclose(np_(taps["topk_weights"]), rw, rtol=WEIGHT_RTOL, atol=0)
-    gs, ge, gn = align_prefix(taps["sorted_ids"], taps["expert_ids"], taps["ntpp"], 128)
-    rs, re_, rn = ref_align.moe_align(rids, E, 128)
+    bm = taps["block_m"]
+    gs, ge, gn = align_prefix(taps["sorted_ids"], taps["expert_ids"], taps["ntpp"], bm)
+    rs, re_, rn = ref_align.moe_align(rids, E, bm)
     assert gn == rn and np.array_equal(gs, rs) and np.array_equal(ge, re_), "layout"
     xq, _, xe = ref_quant.per_token_group_quant_pow2(x_np, 32)
     assert np.array_equal(np_(taps["xq"]), xq) and np.array_equal(np_(taps["xs"]), xe), "x codes"
@@ -83,10 +84,11 @@ def _requant_of_pairs(taps, rows, pairs, P):
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [
-    (5, 256, 256, 8, 2),       # decode-sized, mostly padding blocks
-    (37, 256, 384, 4, 4),      # top_k = E
-    (300, 384, 256, 2, 1),     # several blocks per expert
-    (64, 512, 512, 16, 3),
+    (5, 256, 256, 8, 2),       # 16-row blocks
+    (37, 256, 384, 4, 4),      # top_k = E, 64-row blocks (two 32-row halves)
+    (300, 384, 256, 2, 1),     # 128-row blocks, several per expert
+    (64, 512, 512, 16, 3),     # 32-row blocks
+    (20, 256, 256, 64, 6),     # many small experts, heavy padding
 ])
 @pytest.mark.parametrize("spread", [False, True])
 def test_mx_small_layers(T, H, I, E, k, spread):
