@@ -11,6 +11,7 @@ constexpr float kFp8Max = 448.0f;    // largest finite e4m3fn magnitude
 constexpr float kAmaxEps = 1e-8f;    // lower clamp of a group amax
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));

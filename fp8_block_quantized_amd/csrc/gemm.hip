@@ -152,9 +152,7 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
   return r;
 }
 
-// kMx: MXFP8 operands (exponent bytes per row and 32 K elements, applied by
-// the MFMA itself; the accumulator runs through it with no fold)
-template <int BM, bool kMx = false>
+template <int BM>
 __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   constexpr int NQ = BM / 16;                  // token sub-tiles
   constexpr int CHUNKS = BM * 8;               // 16-byte chunks of a token tile
@@ -182,14 +180,8 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   for (int pp = 0; pp < 4; ++pp)
     wptr[pp] = wbase + (size_t)(wave_on ? prow[pp] + l16 : l16) * K + g * 16;
   const int nblk_n = args.N >> 7;
-  const float* ws0 = kMx ? nullptr
-                         : args.w_scale + ((size_t)e * nblk_n + (wave_on ? (256 * j + 64 * wave) >> 7 : 0)) * nkb;
-  // MX: this lane's exponent byte of each fragment row, block g of K block kb at + 4 kb
-  const uint8_t* wep[4];
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
-    wep[pp] = (const uint8_t*)args.w_scale +
-              ((size_t)e * args.N + (wave_on ? prow[pp] + l16 : l16)) * (nkb * 4) + g;
+  const float* ws0 =
+      args.w_scale + ((size_t)e * nblk_n + (wave_on ? (256 * j + 64 * wave) >> 7 : 0)) * nkb;
 
   // ---- token side: BM x 128 tile per K block, staged in LDS ----
   const uint8_t* aptr[CPT];
@@ -206,13 +198,11 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
     }
   }
   const float* sptr[NQ];
-  const uint8_t* aep[NQ];
   int qoff0[NQ], qoff1[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int rq = 16 * q + l16;
     sptr[q] = args.act_scale + (size_t)(row0 + rq) * nkb;
-    aep[q] = (const uint8_t*)args.act_scale + (size_t)(row0 + rq) * (nkb * 4) + g;
     qoff0[q] = rq * 128 + ((g ^ (rq & 7)) << 4);
     qoff1[q] = rq * 128 + (((g + 4) ^ (rq & 7)) << 4);
   }
@@ -225,16 +215,9 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) wcur[pp] = load_frag_global(wptr[pp]);
   float sa[NQ];
-  int ew[4], ea[NQ];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    if (kMx) ea[q] = aep[q][0];
-    else sa[q] = sptr[q][0];
-  }
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
-    if (kMx) ew[pp] = wep[pp][0];
-  float sw0 = kMx ? 0.0f : ws0[0];
+  for (int q = 0; q < NQ; ++q) sa[q] = sptr[q][0];
+  float sw0 = ws0[0];
 #pragma unroll
   for (int i = 0; i < CPT; ++i)
     if (soff[i] >= 0) *(uint4*)(&smem[0][soff[i]]) = areg[i];
@@ -259,16 +242,9 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) wnext[pp] = load_frag_global(wptr[pp] + koff);
     float sa_n[NQ];
-    int ew_n[4], ea_n[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if (kMx) ea_n[q] = aep[q][4 * kn];
-      else sa_n[q] = sptr[q][kn];
-    }
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp)
-      if (kMx) ew_n[pp] = wep[pp][4 * kn];
-    const float sw0_n = kMx ? 0.0f : ws0[kn];
+    for (int q = 0; q < NQ; ++q) sa_n[q] = sptr[q][kn];
+    const float sw0_n = ws0[kn];
 
     // MFMAs on K block kb
 #pragma unroll
@@ -278,20 +254,13 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
       v8i bq;
       bq[0] = t0.x; bq[1] = t0.y; bq[2] = t0.z; bq[3] = t0.w;
       bq[4] = t1.x; bq[5] = t1.y; bq[6] = t1.z; bq[7] = t1.w;
-      if (kMx) {
+      const float sc = sa[q] * sw0;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp)
-          acc[pp][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[pp], bq, acc[pp][q], 0, 0,
-                                                                       0, ew[pp], 0, ea[q]);
-      } else {
-        const float sc = sa[q] * sw0;
+      for (int pp = 0; pp < 4; ++pp) {
+        const v4f part =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[pp], bq, zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wcur[pp], bq, zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
-        }
+        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[r], sc, acc[pp][q][r]);
       }
     }
     if (kb + 1 < nkb) {
@@ -301,15 +270,9 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
     }
     __syncthreads();
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      wcur[pp] = wnext[pp];
-      if (kMx) ew[pp] = ew_n[pp];
-    }
+    for (int pp = 0; pp < 4; ++pp) wcur[pp] = wnext[pp];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if (kMx) ea[q] = ea_n[q];
-      else sa[q] = sa_n[q];
-    }
+    for (int q = 0; q < NQ; ++q) sa[q] = sa_n[q];
     sw0 = sw0_n;
   }
 
@@ -1140,128 +1103,242 @@ __global__ __launch_bounds__(512) void moe_gemm1_mx_kernel(GemmArgs args) {
   }
 }
 
-// GEMM1 of the MXFP8 layer at decode sizes (block_m <= 64): the structure of
-// moe_gemm2_kernel (each wave streams its weight rows from HBM into MFMA
-// fragments one K block ahead; the e4m3 token rows, gathered through the
-// sorted layout, are shared through a double-buffered LDS tile), the
-// exponent bytes loaded with their operands and applied by the MFMA, and
-// moe_gemm1_mx_kernel's epilogue: wave w holds the gate and up rows of
-// features 32 w .. 32 w + 31 of the tile's 128, one requant group.
-template <int RM>
-__global__ __launch_bounds__(256) void moe_gemm1_mx_dec_kernel(GemmArgs args, int BM) {
-  constexpr int NQ = RM / 16;
-  constexpr int CHUNKS = RM * 8;               // 16-byte chunks of a token tile
-  constexpr int CPT = (CHUNKS + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][RM * 128];
+// Decode-sized MXFP8 GEMMs (block_m <= 64), register-streamed.
+//
+// At decode sizes the GEMMs read each weight byte once from HBM, and the
+// token rows (a few KB per K block) come from L2.  A workgroup covers 16
+// token rows (a block of BM rows is BM / 16 workgroups, which read the same
+// weights, the later ones from L2), and each of its waves 64 weight rows.
+// Both operands are loaded straight into MFMA fragments (lane (g, l16)
+// takes bytes 16g..16g+15 and 64+16g..64+16g+15 of its row's 128-byte K
+// block, the scaled MFMA's K order) together with the row's exponent byte
+// of 32-element block g.  No LDS and no barrier: every wave runs on its own,
+// and the K loop alternates between two register sets, so the loads of K
+// block kb + 1 are in flight while block kb is multiplied (a single set
+// copied at the end of each step would make the compiler wait for those
+// loads first).  Token rows past the block's real pairs read the first real
+// row instead; their results are never stored.
+struct MxDecStream {
+  const uint8_t* w;      // this wave's weight fragment rows: base of the expert's matrix
+  const uint8_t* we;     // and of its exponent bytes
+  uint32_t woff[4];      // per fragment: row * K + 16 g
+  uint32_t weoff[4];     // per fragment: row * K / 32 + g
+  uint32_t wqoff;        // row l16 of fragment g: row * K / 32 (the 16-byte exponent groups)
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  const TileCoord tc = tile_of(blockIdx.x, args);
-  if (!tc.valid) return;
-  const int b = tc.b, half = tc.half, j = tc.j;
-  const int row0 = b * BM + half * RM;
-  if (load_uniform(args.sorted_ids + row0) >= args.P) return;   // padding only
-  const int e = load_uniform(args.expert_ids + b);
-  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * j;
+// Buffer descriptor word 3 for raw byte-addressed buffers on CDNA
+// (32-bit data format, no swizzle, range checking on the byte offset).
+constexpr int kBufferWord3 = 0x00020000;
 
-  const uint8_t* wptr[4];
-  const uint8_t* wep[4];
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    const int row = (pp < 2 ? 0 : I) + i0 + 32 * wave + 16 * (pp & 1) + l16;
-    wptr[pp] = args.w + ((size_t)e * args.N + row) * K + g * 16;
-    wep[pp] = (const uint8_t*)args.w_scale + ((size_t)e * args.N + row) * (nkb * 4) + g;
-  }
-  const uint8_t* aptr[CPT];
-  int soff[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = tid + 256 * i;
-    aptr[i] = nullptr;
-    soff[i] = -1;
-    if (c < CHUNKS) {
-      const int r = c >> 3, ch = c & 7;
-      soff[i] = r * 128 + ((ch ^ (r & 7)) << 4);
-      const int p = args.sorted_ids[row0 + r];
-      if (p < args.P) aptr[i] = args.act + (size_t)(p / args.top_k) * K + ch * 16;
-    }
-  }
-  const uint8_t* aep[NQ];
-  int qoff0[NQ], qoff1[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int rq = 16 * q + l16;
-    const int p = args.sorted_ids[row0 + rq];
-    aep[q] = p < args.P ? (const uint8_t*)args.act_scale + (size_t)(p / args.top_k) * (nkb * 4) + g
-                        : nullptr;
-    qoff0[q] = rq * 128 + ((g ^ (rq & 7)) << 4);
-    qoff1[q] = rq * 128 + (((g + 4) ^ (rq & 7)) << 4);
-  }
+template <int NQ>
+struct MxDecRegs {
+  v8i w[4];
+  v8i t[NQ];
+  int ew[4];
+  int et[NQ];
+};
 
-  uint4 areg[CPT];
+template <int NQ>
+__device__ __forceinline__ void mx_dec_load(MxDecRegs<NQ>& r, const MxDecStream& s,
+                                            const uint8_t* const (&tptr)[NQ],
+                                            const uint8_t* const (&tep)[NQ], int kb) {
+  const uint32_t ko = (uint32_t)kb * 128;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) areg[i] = aptr[i] ? *(const uint4*)aptr[i] : make_uint4(0, 0, 0, 0);
-  v8i wcur[4];
-  int ew[4], ea[NQ];
+  for (int pp = 0; pp < 4; ++pp) r.w[pp] = load_frag_global(s.w + s.woff[pp] + ko);
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    wcur[pp] = load_frag_global(wptr[pp]);
-    ew[pp] = wep[pp][0];
-  }
+  for (int q = 0; q < NQ; ++q) r.t[q] = load_frag_global(tptr[q] + ko);
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) ea[q] = aep[q] ? aep[q][0] : 127;
+  for (int pp = 0; pp < 4; ++pp) r.ew[pp] = s.we[s.weoff[pp] + 4 * kb];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i)
-    if (soff[i] >= 0) *(uint4*)(&smem[0][soff[i]]) = areg[i];
-  __syncthreads();
+  for (int q = 0; q < NQ; ++q) r.et[q] = tep[q][4 * kb];
+}
 
-  v4f acc[4][NQ];
+template <int NQ>
+__device__ __forceinline__ void mx_dec_mma(v4f (&acc)[4][NQ], const MxDecRegs<NQ>& r) {
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+      acc[pp][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.w[pp], r.t[q], acc[pp][q], 0, 0,
+                                                                   0, r.ew[pp], 0, r.et[q]);
+}
+
+// acc[pp][q] += W[rows of fragment pp] . T[token rows of q] over all nkb K blocks
+template <int NQ>
+__device__ __forceinline__ void mx_dec_kloop(v4f (&acc)[4][NQ], const MxDecStream& s,
+                                             const uint8_t* const (&tptr)[NQ],
+                                             const uint8_t* const (&tep)[NQ], int nkb) {
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
     for (int q = 0; q < NQ; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
+  // the scheduling barriers keep each load group ahead of the MFMAs it
+  // overlaps (the scheduler would otherwise sink the loads below them)
+  MxDecRegs<NQ> ra, rb;
+  mx_dec_load(ra, s, tptr, tep, 0);
+  int kb = 0;
+  for (; kb + 2 <= nkb; kb += 2) {
+    mx_dec_load(rb, s, tptr, tep, kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_dec_mma(acc, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    // the last even step re-reads block nkb - 1 (an L2 hit) rather than branch
+    mx_dec_load(ra, s, tptr, tep, kb + 2 < nkb ? kb + 2 : nkb - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_dec_mma(acc, rb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kb < nkb) mx_dec_mma(acc, ra);   // odd nkb: block nkb - 1, loaded into ra
+}
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    const int kn = kb + 1 < nkb ? kb + 1 : kb;     // the last prefetch re-reads
-    const size_t koff = (size_t)kn * 128;
+// The same loop for K a multiple of 512 with 16-byte aligned weight
+// exponents: the exponent bytes of a weight row for four K blocks are one
+// aligned 16-byte group.  Lane (g, l16) loads the group of row l16 of
+// fragment g once per four K blocks, two steps before the next group's first
+// use (its last word is kept aside for the group's last step), and the lane
+// that multiplies fragment pp takes word d of lane (pp, l16)'s group with
+// ds_bpermute and its byte g.  The weight exponents then cost one load per
+// four K blocks instead of four per block.  The weights and their exponents
+// are read through buffer descriptors over the expert's matrices (a 32-bit
+// lane offset and the K step as the scalar offset; reads past the matrix
+// would return zeros), which with the above leaves few enough registers for
+// four waves per SIMD.
+template <int NQ>
+struct MxDecRegs4 {
+  v8i w[4];
+  v8i t[NQ];
+  int et[NQ];
+};
+
+struct MxDecBuf {
+  __amdgpu_buffer_rsrc_t w, we;   // the expert's weights and weight exponents
+  uint32_t woff[4];               // per fragment: row * K + 16 g
+  uint32_t wqoff;                 // row l16 of fragment g: row * K / 32
+};
+
+__device__ __forceinline__ v8i load_frag_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
+  const v4u a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+  const v4u b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff + 64, 0);
+  v8i r;
+  r[0] = (int)a[0]; r[1] = (int)a[1]; r[2] = (int)a[2]; r[3] = (int)a[3];
+  r[4] = (int)b[0]; r[5] = (int)b[1]; r[6] = (int)b[2]; r[7] = (int)b[3];
+  return r;
+}
+
+template <int NQ>
+__device__ __forceinline__ void mx_dec_load4(MxDecRegs4<NQ>& r, const MxDecBuf& s,
+                                             const uint8_t* const (&tptr)[NQ],
+                                             const uint8_t* const (&tep)[NQ], int kb) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      areg[i] = aptr[i] ? *(const uint4*)(aptr[i] + koff) : make_uint4(0, 0, 0, 0);
-    v8i wnext[4];
-    int ew_n[4], ea_n[NQ];
+  for (int pp = 0; pp < 4; ++pp) r.w[pp] = load_frag_buf(s.w, s.woff[pp], kb * 128);
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      wnext[pp] = load_frag_global(wptr[pp] + koff);
-      ew_n[pp] = wep[pp][4 * kn];
-    }
+  for (int q = 0; q < NQ; ++q) r.t[q] = load_frag_global(tptr[q] + (size_t)kb * 128);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) ea_n[q] = aep[q] ? aep[q][4 * kn] : 127;
+  for (int q = 0; q < NQ; ++q) r.et[q] = tep[q][4 * kb];
+}
+
+// word: this K block's word of the exponent group held by this lane
+template <int NQ>
+__device__ __forceinline__ void mx_dec_mma4(v4f (&acc)[4][NQ], const MxDecRegs4<NQ>& r, int word) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+  int ew[4];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const uint4 t0 = *(const uint4*)(&smem[buf][qoff0[q]]);
-      const uint4 t1 = *(const uint4*)(&smem[buf][qoff1[q]]);
-      v8i bq;
-      bq[0] = t0.x; bq[1] = t0.y; bq[2] = t0.z; bq[3] = t0.w;
-      bq[4] = t1.x; bq[5] = t1.y; bq[6] = t1.z; bq[7] = t1.w;
+  for (int pp = 0; pp < 4; ++pp)
+    ew[pp] = (__builtin_amdgcn_ds_bpermute((16 * pp + l16) << 2, word) >> (8 * g)) & 0xff;
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
-        acc[pp][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[pp], bq, acc[pp][q], 0, 0, 0,
-                                                                     ew[pp], 0, ea[q]);
-    }
-    if (kb + 1 < nkb) {
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
-      for (int i = 0; i < CPT; ++i)
-        if (soff[i] >= 0) *(uint4*)(&smem[buf ^ 1][soff[i]]) = areg[i];
-    }
-    __syncthreads();
+    for (int pp = 0; pp < 4; ++pp)
+      acc[pp][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(r.w[pp], r.t[q], acc[pp][q], 0, 0,
+                                                                   0, ew[pp], 0, r.et[q]);
+}
+
+template <int NQ>
+__device__ __forceinline__ void mx_dec_kloop4(v4f (&acc)[4][NQ], const MxDecBuf& s,
+                                              const uint8_t* const (&tptr)[NQ],
+                                              const uint8_t* const (&tep)[NQ], int nkb) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      wcur[pp] = wnext[pp];
-      ew[pp] = ew_n[pp];
-    }
+  for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) ea[q] = ea_n[q];
+    for (int q = 0; q < NQ; ++q) acc[pp][q] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4u wq = __builtin_amdgcn_raw_buffer_load_b128(s.we, s.wqoff, 0, 0);
+  MxDecRegs4<NQ> ra, rb;
+  mx_dec_load4(ra, s, tptr, tep, 0);
+  for (int kb = 0; kb < nkb; kb += 4) {
+    mx_dec_load4(rb, s, tptr, tep, kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_dec_mma4(acc, ra, (int)wq[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_dec_load4(ra, s, tptr, tep, kb + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_dec_mma4(acc, rb, (int)wq[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_dec_load4(rb, s, tptr, tep, kb + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_dec_mma4(acc, ra, (int)wq[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    // the last group re-reads block nkb - 1 and its own exponents rather than branch
+    const int w3 = (int)wq[3];
+    const int kn = kb + 4 < nkb ? kb + 4 : kb;
+    wq = __builtin_amdgcn_raw_buffer_load_b128(s.we, s.wqoff, 4 * kn, 0);
+    mx_dec_load4(ra, s, tptr, tep, kb + 4 < nkb ? kb + 4 : nkb - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mx_dec_mma4(acc, rb, w3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// GEMM1: wave w holds the gate and up rows of features 32 w .. 32 w + 31 of
+// the workgroup's 128-feature tile j (fragments pp = 0, 1 gate, 2, 3 up), so
+// SiLU*mul pairs in-lane and each token's 32-feature requant group is reduced
+// over the wave's four lane groups.  A block of BM rows is covered by
+// BM / 16 workgroups.
+template <bool kQuad>
+__global__ __launch_bounds__(256) void moe_gemm1_mx_dec_kernel(GemmArgs args, int BM) {
+  constexpr int RM = 16, NQ = 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const TileCoord tc = tile_of(blockIdx.x, args);
+  if (!tc.valid) return;
+  const int row0 = tc.b * BM + tc.half * RM;
+  const int p0 = load_uniform(args.sorted_ids + row0);
+  if (p0 >= args.P) return;   // padding only
+  const int e = load_uniform(args.expert_ids + tc.b);
+  const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * tc.j;
+
+  MxDecStream s;
+  s.w = args.w + (size_t)e * args.N * K;
+  s.we = (const uint8_t*)args.w_scale + (size_t)e * args.N * (nkb * 4);
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int row = (pp < 2 ? 0 : I) + i0 + 32 * wave + 16 * (pp & 1) + l16;
+    s.woff[pp] = (uint32_t)row * K + 16 * g;
+    s.weoff[pp] = (uint32_t)row * (nkb * 4) + g;
+  }
+  s.wqoff = (uint32_t)((g < 2 ? 0 : I) + i0 + 32 * wave + 16 * (g & 1) + l16) * (nkb * 4);
+  const uint32_t wbytes = (uint32_t)args.N * K;
+  const uint8_t* tptr[NQ];
+  const uint8_t* tep[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    int p = args.sorted_ids[row0 + 16 * q + l16];
+    if (p >= args.P) p = p0;
+    const size_t tok = (size_t)(p / args.top_k);
+    tptr[q] = args.act + tok * K + 16 * g;
+    tep[q] = (const uint8_t*)args.act_scale + tok * (nkb * 4) + g;
+  }
+
+  v4f acc[4][NQ];
+  if (kQuad) {
+    MxDecBuf b;
+    b.w = __builtin_amdgcn_make_buffer_rsrc((void*)s.w, 0, (int)wbytes, kBufferWord3);
+    b.we = __builtin_amdgcn_make_buffer_rsrc((void*)s.we, 0, (int)(wbytes / 32), kBufferWord3);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) b.woff[pp] = s.woff[pp];
+    b.wqoff = s.wqoff;
+    mx_dec_kloop4(acc, b, tptr, tep, nkb);
+  } else {
+    mx_dec_kloop(acc, s, tptr, tep, nkb);
   }
 
   // a = silu(gate) * up, requantised per token row and 32-feature group;
@@ -1295,6 +1372,80 @@ __global__ __launch_bounds__(256) void moe_gemm1_mx_dec_kernel(GemmArgs args, in
   }
 }
 
+// GEMM2: wave w holds output features 256 j + 64 w .. + 63 (fragments of 16
+// rows), bf16 y for each sorted row of a real pair (the combine applies the
+// routing weight).  The sorted activation rows are dense, so token rows are
+// rows row0 .. row0 + RM - 1 of act.  The last tile of an H that is not a
+// multiple of 256 has idle waves, which leave at once.
+template <bool kQuad>
+__global__ __launch_bounds__(256) void moe_gemm2_mx_dec_kernel(GemmArgs args, int BM) {
+  constexpr int RM = 16, NQ = 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const TileCoord tc = tile_of(blockIdx.x, args);
+  if (!tc.valid) return;
+  const int row0 = tc.b * BM + tc.half * RM;
+  if (load_uniform(args.sorted_ids + row0) >= args.P) return;   // padding only
+  const int h0 = 256 * tc.j + 64 * wave;
+  if (h0 >= args.N) return;
+  const int e = load_uniform(args.expert_ids + tc.b);
+  const int K = args.K, nkb = K >> 7;
+
+  MxDecStream s;
+  s.w = args.w + (size_t)e * args.N * K;
+  s.we = (const uint8_t*)args.w_scale + (size_t)e * args.N * (nkb * 4);
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int row = h0 + 16 * pp + l16;
+    s.woff[pp] = (uint32_t)row * K + 16 * g;
+    s.weoff[pp] = (uint32_t)row * (nkb * 4) + g;
+  }
+  s.wqoff = (uint32_t)(h0 + 16 * g + l16) * (nkb * 4);
+  const uint32_t wbytes = (uint32_t)args.N * K;
+  const uint8_t* tptr[NQ];
+  const uint8_t* tep[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    int r = row0 + 16 * q + l16;
+    if (args.sorted_ids[r] >= args.P) r = row0;
+    tptr[q] = args.act + (size_t)r * K + 16 * g;
+    tep[q] = (const uint8_t*)args.act_scale + (size_t)r * (nkb * 4) + g;
+  }
+
+  v4f acc[4][NQ];
+  if (kQuad) {
+    MxDecBuf b;
+    b.w = __builtin_amdgcn_make_buffer_rsrc((void*)s.w, 0, (int)wbytes, kBufferWord3);
+    b.we = __builtin_amdgcn_make_buffer_rsrc((void*)s.we, 0, (int)(wbytes / 32), kBufferWord3);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) b.woff[pp] = s.woff[pp];
+    b.wqoff = s.wqoff;
+    mx_dec_kloop4(acc, b, tptr, tep, nkb);
+  } else {
+    mx_dec_kloop(acc, s, tptr, tep, nkb);
+  }
+
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int r = row0 + 16 * q + l16;
+    if (args.sorted_ids[r] >= args.P) continue;
+    uint16_t* yrow = args.y_out + (size_t)r * args.y_stride;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      uint2 v;
+      v.x = f32_to_bf16_bits(acc[pp][q][0]) | (f32_to_bf16_bits(acc[pp][q][1]) << 16);
+      v.y = f32_to_bf16_bits(acc[pp][q][2]) | (f32_to_bf16_bits(acc[pp][q][3]) << 16);
+      *(uint2*)(yrow + h0 + 16 * pp + 4 * g) = v;
+    }
+  }
+}
+
+// The decode MXFP8 kernels' 16-byte weight exponent groups: K a multiple of
+// 512 and the exponent array 16-byte aligned.
+static bool mx_quad_ok(const GemmArgs& a) {
+  return (a.K >> 7) % 4 == 0 && (uintptr_t)a.w_scale % 16 == 0;
+}
+
 hipError_t launch_gemm1_mx(const uint8_t* xq, const uint8_t* xe, const uint8_t* w13,
                            const uint8_t* w13e, const int32_t* sorted_ids, const int32_t* expert_ids,
                            const int32_t* ntpp, const int32_t* eoff, int E, int H, int I, int P,
@@ -1310,15 +1461,13 @@ hipError_t launch_gemm1_mx(const uint8_t* xq, const uint8_t* xe, const uint8_t* 
     hipLaunchKernelGGL(moe_gemm1_mx_kernel, dim3((unsigned)(nblk * a.n_tiles)), dim3(512), 0, stream, a);
     return hipGetLastError();
   }
-  const int rm = BM < 32 ? BM : 32;
-  a.split = BM / rm;
+  if (BM < 16 || BM > 64) return hipErrorInvalidValue;
+  a.split = BM / 16;
   const dim3 grid((unsigned)(nblk * a.split * a.n_tiles)), block(256);
-  if (rm == 16)
-    hipLaunchKernelGGL(moe_gemm1_mx_dec_kernel<16>, grid, block, 0, stream, a, BM);
-  else if (rm == 32)
-    hipLaunchKernelGGL(moe_gemm1_mx_dec_kernel<32>, grid, block, 0, stream, a, BM);
+  if (mx_quad_ok(a))
+    hipLaunchKernelGGL(moe_gemm1_mx_dec_kernel<true>, grid, block, 0, stream, a, BM);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL(moe_gemm1_mx_dec_kernel<false>, grid, block, 0, stream, a, BM);
   return hipGetLastError();
 }
 
@@ -1356,12 +1505,14 @@ static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream)
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
   const bool persistent = BM == 128 && (a.K >> 7) / a.ksplit >= 2;
   if (a.mx && !persistent) {       // exponent scales: the persistent kernel, or the decode ones
-    switch (BM) {
-      case 16: hipLaunchKernelGGL((moe_gemm2_kernel<16, true>), grid, block, 0, stream, a); break;
-      case 32: hipLaunchKernelGGL((moe_gemm2_kernel<32, true>), grid, block, 0, stream, a); break;
-      case 64: hipLaunchKernelGGL((moe_gemm2_kernel<64, true>), grid, block, 0, stream, a); break;
-      default: return hipErrorInvalidValue;
-    }
+    if (BM > 64 || a.ksplit != 1) return hipErrorInvalidValue;
+    GemmArgs d = a;
+    d.split = BM / 16;
+    const dim3 g2((unsigned)(d.nblk * d.split * d.n_tiles));
+    if (mx_quad_ok(d))
+      hipLaunchKernelGGL(moe_gemm2_mx_dec_kernel<true>, g2, block, 0, stream, d, BM);
+    else
+      hipLaunchKernelGGL(moe_gemm2_mx_dec_kernel<false>, g2, block, 0, stream, d, BM);
     return hipGetLastError();
   }
   if (persistent) {
