@@ -27,7 +27,8 @@
 //   * decode (BM <= 64): each wave streams its private weight rows from HBM
 //     straight into MFMA fragments one K block ahead; the token tile of a K
 //     block is shared by the workgroup's waves through an XOR-swizzled,
-//     double-buffered LDS tile;
+//     double-buffered LDS tile (the MXFP8 decode kernels instead load the
+//     token fragments per wave too, with no LDS);
 //   * prefill (BM = 128): 128 rows x 256 weight rows per tile, 8 waves of
 //     64 x 64, operands staged through a three-stage LDS ring filled by
 //     direct global->LDS loads with hand-placed vmcnt waits; GEMM2 and the
