@@ -85,9 +85,11 @@ def _requant_of_pairs(taps, rows, pairs, P):
 
 @pytest.mark.parametrize("T,H,I,E,k", [
     (5, 256, 256, 8, 2),       # 16-row blocks
-    (37, 256, 384, 4, 4),      # top_k = E, 64-row blocks (two 32-row halves)
+    (37, 256, 384, 4, 4),      # top_k = E, 64-row blocks (four 16-row workgroups), odd K blocks
     (300, 384, 256, 2, 1),     # 128-row blocks, several per expert
-    (64, 512, 512, 16, 3),     # 32-row blocks
+    (64, 512, 512, 16, 3),     # 32-row blocks, exponents in 16-byte groups (K % 512 == 0)
+    (64, 512, 1024, 4, 2),     # 64-row blocks on the 16-byte exponent groups, 8 K blocks in GEMM2
+    (40, 1024, 640, 8, 2),     # grouped exponents in GEMM1, per-block bytes in GEMM2 (5 K blocks)
     (20, 256, 256, 64, 6),     # many small experts, heavy padding
 ])
 @pytest.mark.parametrize("spread", [False, True])
@@ -117,6 +119,39 @@ def test_mx_small_layers(T, H, I, E, k, spread):
     else:
         m = assert_out_close(o, ref, "mx small")
         note(f"  max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e} requant_differing={mm:.2e}")
+
+
+def _misaligned_copy(t):
+    """t's bytes at an address 4 bytes past a 16-byte boundary (the C ABI
+    asks 4-byte alignment of the exponent arrays)"""
+    buf = torch.empty(t.numel() + 16, dtype=torch.uint8, device="cuda")
+    base = (-buf.data_ptr()) % 16
+    v = buf[base + 4:base + 4 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 == 4
+    return v
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(6, 512, 512, 8, 2), (64, 512, 1024, 4, 2)])
+def test_mx_misaligned_exponents_match(T, H, I, E, k):
+    """With K a multiple of 512 the decode GEMMs read the weight exponents in
+    aligned 16-byte groups; exponent arrays that are only 4-byte aligned take
+    the per-block byte loads instead.  Both apply the same exponents to the
+    same MFMAs, so the requantised activation and the output are identical."""
+    note(f"mx forward misaligned exponents T={T} H={H} I={I} E={E} k={k}")
+    w13, w13e, w2, w2e = (a.cuda() for a in make_mx_weights(H, I, E, 31 + T))
+    x, logits = (a.cuda() for a in make_activations(H, E, T, 310 + T))
+    out_a, taps_a = _run(x, logits, [w13, w13e, w2, w2e], T, H, I, E, k)
+    out_b, taps_b = _run(x, logits, [w13, _misaligned_copy(w13e), w2, _misaligned_copy(w2e)],
+                         T, H, I, E, k)
+    assert taps_a["block_m"] <= 64, "decode-sized blocks expected"
+    # the rows of real pairs (padding rows are never written)
+    bm, P = taps_a["block_m"], T * k
+    rows, _, _ = align_prefix(taps_a["sorted_ids"], taps_a["expert_ids"], taps_a["ntpp"], bm)
+    ga, gea = _requant_of_pairs(taps_a, rows, np.arange(P), P)
+    gb, geb = _requant_of_pairs(taps_b, rows, np.arange(P), P)
+    assert np.array_equal(ga, gb) and np.array_equal(gea, geb), "requantised rows differ"
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16)), "outputs differ"
 
 
 @pytest.mark.parametrize("T", [64, 8192])
