@@ -153,7 +153,11 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
   return r;
 }
 
-template <int BM>
+// kSlices: the workgroups of a tile (TileCoord::half, args.split of them)
+// each reduce one contiguous range of K blocks and store float32 partials by
+// pair, part[slice][p][:] (the combine sums the slices in order); without it
+// one workgroup covers all of K and stores the bf16 y row.
+template <int BM, bool kSlices>
 __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   constexpr int NQ = BM / 16;                  // token sub-tiles
   constexpr int CHUNKS = BM * 8;               // 16-byte chunks of a token tile
@@ -166,7 +170,10 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   if (!tc.valid) return;
   const int b = tc.b, j = tc.j;
   const int e = load_uniform(args.expert_ids + b);
-  const int K = args.K, nkb = K >> 7;
+  const int K = args.K, nkb_all = K >> 7;
+  // this workgroup's K blocks [kb0, kb0 + nkb)
+  const int kb0 = kSlices ? (int)((long long)tc.half * nkb_all / args.split) : 0;
+  const int nkb = kSlices ? (int)((long long)(tc.half + 1) * nkb_all / args.split) - kb0 : nkb_all;
   const int row0 = b * BM;
 
   // ---- weight side: 4 fragments of 16 rows per wave ----
@@ -175,14 +182,14 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   int prow[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) prow[pp] = 256 * j + 64 * wave + 16 * pp;
-  const uint8_t* wbase = args.w + (size_t)e * args.N * K;
+  const uint8_t* wbase = args.w + (size_t)e * args.N * K + (size_t)kb0 * 128;
   const uint8_t* wptr[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp)
     wptr[pp] = wbase + (size_t)(wave_on ? prow[pp] + l16 : l16) * K + g * 16;
   const int nblk_n = args.N >> 7;
   const float* ws0 =
-      args.w_scale + ((size_t)e * nblk_n + (wave_on ? (256 * j + 64 * wave) >> 7 : 0)) * nkb;
+      args.w_scale + ((size_t)e * nblk_n + (wave_on ? (256 * j + 64 * wave) >> 7 : 0)) * nkb_all + kb0;
 
   // ---- token side: BM x 128 tile per K block, staged in LDS ----
   const uint8_t* aptr[CPT];
@@ -195,7 +202,7 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
     if (c < CHUNKS) {
       const int r = c >> 3, ch = c & 7;
       soff[i] = r * 128 + ((ch ^ (r & 7)) << 4);
-      aptr[i] = args.act + (size_t)(row0 + r) * K + ch * 16;
+      aptr[i] = args.act + (size_t)(row0 + r) * K + (size_t)kb0 * 128 + ch * 16;
     }
   }
   const float* sptr[NQ];
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int rq = 16 * q + l16;
-    sptr[q] = args.act_scale + (size_t)(row0 + rq) * nkb;
+    sptr[q] = args.act_scale + (size_t)(row0 + rq) * nkb_all + kb0;
     qoff0[q] = rq * 128 + ((g ^ (rq & 7)) << 4);
     qoff1[q] = rq * 128 + (((g + 4) ^ (rq & 7)) << 4);
   }
@@ -278,12 +285,22 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
   }
 
   // y of each sorted row of a real pair, bf16 (the combine applies the
-  // routing weight)
+  // routing weight); with K slices the float32 partial of the pair's row
   if (!wave_on) return;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int rq = 16 * q + l16;
-    if (args.sorted_ids[row0 + rq] >= args.P) continue;
+    const int p = args.sorted_ids[row0 + rq];
+    if (p >= args.P) continue;
+    if (kSlices) {
+      float* prow_out = args.part + ((size_t)tc.half * args.P + p) * args.y_stride;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int h0 = 256 * j + 64 * wave + 16 * pp + 4 * g;
+        *(float4*)(prow_out + h0) = make_float4(acc[pp][q][0], acc[pp][q][1], acc[pp][q][2], acc[pp][q][3]);
+      }
+      continue;
+    }
     uint16_t* yrow = args.y_out + (size_t)(row0 + rq) * args.y_stride;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
@@ -1536,11 +1553,21 @@ static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream)
       hipLaunchKernelGGL((moe_gemm2_pf_kernel<false, false>), dim3((unsigned)wg), dim3(512), 0, stream, a);
     return hipGetLastError();
   }
+  if (a.split > 1) {               // K slices of the decode kernel, float32 partials by pair
+    const dim3 gs((unsigned)(a.nblk * a.split * a.n_tiles));
+    switch (BM) {
+      case 16: hipLaunchKernelGGL((moe_gemm2_kernel<16, true>), gs, block, 0, stream, a); break;
+      case 32: hipLaunchKernelGGL((moe_gemm2_kernel<32, true>), gs, block, 0, stream, a); break;
+      case 64: hipLaunchKernelGGL((moe_gemm2_kernel<64, true>), gs, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (BM) {
-    case 16: hipLaunchKernelGGL(moe_gemm2_kernel<16>, grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL(moe_gemm2_kernel<32>, grid, block, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL(moe_gemm2_kernel<64>, grid, block, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(moe_gemm2_kernel<128>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((moe_gemm2_kernel<16, false>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((moe_gemm2_kernel<32, false>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((moe_gemm2_kernel<64, false>), grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((moe_gemm2_kernel<128, false>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1579,9 +1606,12 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
-                        uint16_t* y, int y_stride, hipStream_t stream) {
+                        uint16_t* y, int y_stride, int kslices, float* y_slices,
+                        hipStream_t stream) {
+  if (kslices > 1 && (BM > 64 || !y_slices || kslices > (I >> 7))) return hipErrorInvalidValue;
   GemmArgs a{};
-  a.eoff = eoff; a.E = E; a.split = 1;
+  a.eoff = eoff; a.E = E; a.split = kslices > 1 ? kslices : 1;
+  a.part = y_slices;
   a.act = aq; a.act_scale = as; a.w = w2; a.w_scale = w2s;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
   a.y_out = y; a.y_stride = y_stride;

@@ -32,10 +32,14 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
                         uint8_t* aq, float* as, hipStream_t stream);
+// kslices > 1 (block_m <= 64, at most I/128 slices): the workgroups of a tile
+// split K and store float32 partials by pair, y_slices [kslices, P, y_stride],
+// for launch_combine_slices; otherwise bf16 y by sorted row
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
-                        uint16_t* y, int y_stride, hipStream_t stream);
+                        uint16_t* y, int y_stride, int kslices, float* y_slices,
+                        hipStream_t stream);
 // The MXFP8 layer's GEMMs (block_m 16 to 128): exponent bytes [rows, K/32]
 // for the activations, [E, N, K/32] for the weights; GEMM1 writes the
 // requantised activation's exponent bytes [cap, I/32] into ae
@@ -69,5 +73,10 @@ hipError_t launch_batched_layout(const int32_t* counts, int E, int M, int BM, in
 hipError_t launch_combine(const uint16_t* y, int y_stride, const int32_t* pair_pos,
                           const float* topk_w, int T, int H, int top_k, uint16_t* out,
                           hipStream_t stream);
+// the combine over launch_gemm2's float32 K-slice partials (pairs with
+// pair_pos -1 contribute zero)
+hipError_t launch_combine_slices(const float* part, int y_stride, int nslice, int P,
+                                 const int32_t* pair_pos, const float* topk_w, int T, int H,
+                                 int top_k, uint16_t* out, hipStream_t stream);
 
 }  // namespace moe

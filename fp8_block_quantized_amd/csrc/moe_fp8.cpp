@@ -37,8 +37,29 @@ int pick_block_m(int T, int E, int top_k) {
   return bm;
 }
 
+// K slices of the decode GEMM2 (block_m <= 64): when the weight tiles in use
+// (at most one block per expert plus ceil(P / block_m) more, times ceil(H / 256)
+// tiles of output features) would not give every CU of a 256-CU part four
+// workgroups, each tile's K is split over up to 8 workgroups (at most one per
+// 128-wide K block) that store float32 partials.  A function of the shape
+// alone, so the workspace size is known before anything runs.
+int pick_kslices(int T, int H, int I, int E, int top_k, int BM) {
+  if (BM > 64) return 1;
+  const long long P = (long long)T * top_k;
+  const long long cap_blocks = (P + (long long)E * (BM - 1) + BM - 1) / BM;
+  long long live = (P + BM - 1) / BM + (E < P ? E : P);
+  if (live > cap_blocks) live = cap_blocks;
+  const long long tiles = live * ((H + 255) / 256), want = 4 * 256;
+  if (tiles >= want) return 1;
+  long long s = (want + tiles - 1) / tiles;
+  if (s > 8) s = 8;
+  if (s > I / 128) s = I / 128;
+  return (int)s;
+}
+
 struct Layout {
   int BM;
+  int kslices;       // K slices of GEMM2 (1: bf16 y by sorted row)
   size_t cap;
   size_t off[MOE_TAP_COUNT];
   size_t total;
@@ -46,10 +67,13 @@ struct Layout {
 
 // block_m 0: the forward's choice; the MXFP8 layer passes 128.  The
 // activation scale regions hold float32 per 128 elements or, at the same
-// size, exponent bytes per 32.
-void make_layout(int T, int H, int I, int E, int top_k, Layout& L, int block_m = 0) {
+// size, exponent bytes per 32.  slices: room for GEMM2's K-slice partials
+// (the forward's layout; the batched and MXFP8 paths do not split K).
+void make_layout(int T, int H, int I, int E, int top_k, Layout& L, int block_m = 0,
+                 bool slices = true) {
   const size_t P = (size_t)T * top_k;
   L.BM = block_m ? block_m : pick_block_m(T, E, top_k);
+  L.kslices = slices ? pick_kslices(T, H, I, E, top_k, L.BM) : 1;
   L.cap = round_up(P + (size_t)E * (L.BM - 1), L.BM);
   size_t sz[MOE_TAP_COUNT];
   sz[MOE_TAP_TOPK_IDS] = P * 4;
@@ -64,6 +88,7 @@ void make_layout(int T, int H, int I, int E, int top_k, Layout& L, int block_m =
   sz[MOE_TAP_AS] = L.cap * (I / 128) * 4;
   sz[MOE_TAP_Y] = L.cap * y_stride(H) * 2;
   sz[MOE_TAP_ALIGN_SCRATCH] = moe::align_scratch_bytes((int)P, E);
+  sz[MOE_TAP_Y_SLICES] = L.kslices > 1 ? (size_t)L.kslices * P * y_stride(H) * 4 : 0;
   size_t o = 0;
   for (int i = 0; i < MOE_TAP_COUNT; ++i) {
     L.off[i] = o;
@@ -257,12 +282,17 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
                                top_k, L.BM, nblk, aq, as, stream)))
     return MOE_ERR_HIP;
   if (mark(4)) return MOE_ERR_HIP;
+  float* yslices = (float*)(ws + L.off[MOE_TAP_Y_SLICES]);
   if ((err = moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, EL, H, I, P, L.BM,
-                               nblk, y, (int)y_stride(H), stream)))
+                               nblk, y, (int)y_stride(H), L.kslices, yslices, stream)))
     return MOE_ERR_HIP;
   if (mark(5)) return MOE_ERR_HIP;
-  if ((err = moe::launch_combine(y, (int)y_stride(H), ppos, tw, T, H, top_k, (uint16_t*)out, stream)))
-    return MOE_ERR_HIP;
+  if (L.kslices > 1)
+    err = moe::launch_combine_slices(yslices, (int)y_stride(H), L.kslices, P, ppos, tw, T, H, top_k,
+                                     (uint16_t*)out, stream);
+  else
+    err = moe::launch_combine(y, (int)y_stride(H), ppos, tw, T, H, top_k, (uint16_t*)out, stream);
+  if (err) return MOE_ERR_HIP;
   if (mark(6)) return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -310,7 +340,10 @@ int moe_fp8_forward_traced(const void* x, const float* router_logits, const uint
 // tokens routed to one slot each (token e * max_tokens + r is row r of expert e).
 size_t moe_fp8_batched_workspace_bytes(int E, int max_tokens, int H, int I) {
   if (E < 1 || max_tokens < 1 || (long long)E * max_tokens > MOE_MAX_TOKENS) return 0;
-  return moe_fp8_workspace_bytes(E * max_tokens, H, I, E, 1);
+  if (check_moe_shape(E * max_tokens, H, I, E, 1) != MOE_OK) return 0;
+  Layout L;
+  make_layout(E * max_tokens, H, I, E, 1, L, 0, false);
+  return L.total;
 }
 
 int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, const uint8_t* w13,
@@ -324,7 +357,7 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, con
   if (!x || !expert_num_tokens || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace)
     return MOE_ERR_NULL;
   Layout L;
-  make_layout(T, H, I, E, 1, L);
+  make_layout(T, H, I, E, 1, L, 0, false);
   if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_ERR_WORKSPACE;
   if ((uintptr_t)x % 16 || (uintptr_t)out % 16 || (uintptr_t)w13 % 16 || (uintptr_t)w2 % 16 ||
       (uintptr_t)expert_num_tokens % 4 || (uintptr_t)w13_scale % 4 || (uintptr_t)w2_scale % 4)
@@ -360,7 +393,7 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, con
                         nblk, aq, as, stream))
     return MOE_ERR_HIP;
   if (moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, T, L.BM, nblk, y,
-                        (int)y_stride(H), stream))
+                        (int)y_stride(H), 1, nullptr, stream))
     return MOE_ERR_HIP;
   if (moe::launch_combine(y, (int)y_stride(H), ppos, nullptr, T, H, 1, (uint16_t*)out, stream))
     return MOE_ERR_HIP;
@@ -370,7 +403,7 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, con
 size_t moe_fp8_mx_workspace_bytes(int T, int H, int I, int E, int top_k) {
   if (check_moe_shape(T, H, I, E, top_k) != MOE_OK || I < 256) return 0;
   Layout L;
-  make_layout(T, H, I, E, top_k, L);
+  make_layout(T, H, I, E, top_k, L, 0, false);
   return L.total;
 }
 
@@ -381,7 +414,7 @@ int moe_fp8_mx_workspace_layout(int T, int H, int I, int E, int top_k,
   if (st != MOE_OK) return st;
   if (I < 256) return MOE_ERR_UNSUPPORTED;
   Layout L;
-  make_layout(T, H, I, E, top_k, L);
+  make_layout(T, H, I, E, top_k, L, 0, false);
   for (int i = 0; i < MOE_TAP_COUNT; ++i) offsets[i] = L.off[i];
   return MOE_OK;
 }
@@ -397,7 +430,7 @@ int moe_fp8_mx_forward(const void* x, const float* router_logits, const uint8_t*
   if (renormalize != 0 && renormalize != 1) return MOE_ERR_SHAPE;
   if (I < 256) return MOE_ERR_UNSUPPORTED;
   Layout L;
-  make_layout(T, H, I, E, top_k, L);
+  make_layout(T, H, I, E, top_k, L, 0, false);
   if (workspace_bytes < L.total || ((uintptr_t)workspace % kAlign)) return MOE_ERR_WORKSPACE;
   if ((uintptr_t)x % 16 || (uintptr_t)out % 16 || (uintptr_t)w13 % 16 || (uintptr_t)w2 % 16 ||
       (uintptr_t)router_logits % 4 || (uintptr_t)w13_scale % 4 || (uintptr_t)w2_scale % 4)

@@ -79,8 +79,13 @@ enum {
   MOE_TAP_AQ,               /* uint8 [cap, I] requantised activation, sorted order */
   MOE_TAP_AS,               /* float32 [cap, I/128] its scales */
   MOE_TAP_Y,                /* bf16 [cap, roundup(H, 256)] expert output per sorted row, before
-                               the routing weight (rows of padding undefined) */
+                               the routing weight (rows of padding undefined); unused when
+                               the second GEMM splits K (MOE_TAP_Y_SLICES) */
   MOE_TAP_ALIGN_SCRATCH,    /* int32 scratch of the sort-and-pad stage */
+  MOE_TAP_Y_SLICES,         /* float32 [S, T*top_k, roundup(H, 256)] K-slice partials of the
+                               expert output per pair, summed in slice order by the combine;
+                               S > 1 only for decode shapes whose weight tiles in use would
+                               leave CUs idle (block_m <= 64), else empty */
   MOE_TAP_COUNT
 };
 
@@ -187,8 +192,9 @@ int moe_fp8_forward_routed(const void* x, const float* router_logits,
  *   workspace         moe_fp8_batched_workspace_bytes(E, max_tokens, H, I) bytes,
  *                     256-byte aligned; its MOE_TAP_* tensors are those of
  *                     moe_fp8_workspace_layout(E * max_tokens, H, I, E, 1) with
- *                     token e * max_tokens + r (the router taps are unused, and
- *                     MOE_TAP_ALIGN_SCRATCH holds the expert block offsets)
+ *                     token e * max_tokens + r (the router taps are unused,
+ *                     MOE_TAP_ALIGN_SCRATCH holds the expert block offsets, and
+ *                     the second GEMM does not split K: no MOE_TAP_Y_SLICES)
  * Constraints: E * max_tokens <= MOE_MAX_TOKENS, E <= MOE_MAX_EXPERTS, H and I
  * multiples of 128 as in moe_fp8_forward.
  */
@@ -223,7 +229,8 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens,
  *   out           bf16    [T, H]; must not overlap any input or the workspace
  *   workspace     moe_fp8_mx_workspace_bytes() bytes, 256-byte aligned; its
  *                 MOE_TAP_* tensors at moe_fp8_mx_workspace_layout()'s offsets
- *                 (MOE_TAP_XS and MOE_TAP_AS hold exponent bytes [rows, K/32])
+ *                 (MOE_TAP_XS and MOE_TAP_AS hold exponent bytes [rows, K/32];
+ *                 MOE_TAP_Y_SLICES is empty)
  * Constraints: those of moe_fp8_forward, and I >= 256 (else
  * MOE_ERR_UNSUPPORTED; the workspace query returns 0).
  */

@@ -67,7 +67,7 @@ def test_block_m_choices():
 
 def test_workspace_layout_is_disjoint_and_aligned():
     for shape in [(16, 256, 512, 8, 2), (64, 7168, 2048, 256, 8), (8192, 7168, 2048, 256, 8),
-                  (1, 2048, 768, 128, 8), (512, 4096, 14336, 8, 2)]:
+                  (1, 2048, 768, 128, 8), (512, 4096, 14336, 8, 2), (64, 4096, 14336, 8, 2)]:
         T, H, I, E, k = shape
         off = moe.moe_fp8_workspace_layout(*shape)
         total = moe.moe_fp8_workspace_bytes(*shape)
@@ -81,7 +81,21 @@ def test_workspace_layout_is_disjoint_and_aligned():
         for a, b in zip(names, names[1:]):
             assert off[a] % 256 == 0
             assert off[a] + size[a] <= off[b]
-        assert off[names[-1]] < total
+        # the last region holds the second GEMM's K-slice partials, or nothing
+        ys = -(-H // 256) * 256
+        slices = (total - off["y_slices"]) // (4 * P * ys)
+        assert off["y_slices"] % 256 == 0 and off["y_slices"] + 4 * P * ys * slices <= total
+        assert slices == expect_slices[shape]
+
+
+# K slices of the decode GEMM2: the weight tiles in use (one block per expert
+# plus ceil(P / block_m), times ceil(H / 256)) are raised to 1024 workgroups
+expect_slices = {(16, 256, 512, 8, 2): 4,            # 10 tiles: capped by I / 128 = 4
+                 (64, 7168, 2048, 256, 8): 0,        # 288 blocks x 28 tiles: no split
+                 (8192, 7168, 2048, 256, 8): 0,      # block_m 128: no split
+                 (1, 2048, 768, 128, 8): 6,          # 9 blocks x 8 tiles: capped by I / 128 = 6
+                 (512, 4096, 14336, 8, 2): 0,        # block_m 128
+                 (64, 4096, 14336, 8, 2): 6}         # 12 blocks x 16 tiles -> ceil(1024 / 192)
 
 
 def test_forward_argument_checks():
@@ -236,7 +250,9 @@ def test_batched_argument_checks():
     # every call below is invalid, so it returns before anything is launched
     lib = moe.load_library()
     vp = ctypes.c_void_p
-    assert moe.moe_fp8_batched_workspace_bytes(4, 16, 256, 256) == moe.moe_fp8_workspace_bytes(64, 256, 256, 4, 1)
+    # the forward's layout for E * M tokens at top_k 1, without the K-slice region
+    off = moe.moe_fp8_workspace_layout(64, 256, 256, 4, 1)
+    assert moe.moe_fp8_batched_workspace_bytes(4, 16, 256, 256) == off["y_slices"]
     assert moe.moe_fp8_batched_workspace_bytes(64, 512, 256, 256) == 0          # E * M > 16384
     n = moe.moe_fp8_batched_workspace_bytes(4, 16, 256, 256)
     f = lib.moe_fp8_batched_experts
