@@ -1521,6 +1521,17 @@ static hipError_t launch_reduce_slices(const float* part, int ksplit, int rows, 
 
 static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nblk * a.n_tiles)), block(256);
+  if (a.split > 1) {               // K slices of the register-streaming kernel, float32 partials by pair
+    if (a.mx || a.ksplit != 1) return hipErrorInvalidValue;
+    const dim3 gs((unsigned)(a.nblk * a.split * a.n_tiles));
+    switch (BM) {
+      case 16: hipLaunchKernelGGL((moe_gemm2_kernel<16, true>), gs, block, 0, stream, a); break;
+      case 32: hipLaunchKernelGGL((moe_gemm2_kernel<32, true>), gs, block, 0, stream, a); break;
+      case 64: hipLaunchKernelGGL((moe_gemm2_kernel<64, true>), gs, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const bool persistent = BM == 128 && (a.K >> 7) / a.ksplit >= 2;
   if (a.mx && !persistent) {       // exponent scales: the persistent kernel, or the decode ones
     if (BM > 64 || a.ksplit != 1) return hipErrorInvalidValue;
@@ -1551,16 +1562,6 @@ static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream)
       hipLaunchKernelGGL((moe_gemm2_pf_kernel<true, false>), dim3((unsigned)wg), dim3(512), 0, stream, a);
     else
       hipLaunchKernelGGL((moe_gemm2_pf_kernel<false, false>), dim3((unsigned)wg), dim3(512), 0, stream, a);
-    return hipGetLastError();
-  }
-  if (a.split > 1) {               // K slices of the decode kernel, float32 partials by pair
-    const dim3 gs((unsigned)(a.nblk * a.split * a.n_tiles));
-    switch (BM) {
-      case 16: hipLaunchKernelGGL((moe_gemm2_kernel<16, true>), gs, block, 0, stream, a); break;
-      case 32: hipLaunchKernelGGL((moe_gemm2_kernel<32, true>), gs, block, 0, stream, a); break;
-      case 64: hipLaunchKernelGGL((moe_gemm2_kernel<64, true>), gs, block, 0, stream, a); break;
-      default: return hipErrorInvalidValue;
-    }
     return hipGetLastError();
   }
   switch (BM) {

@@ -84,8 +84,8 @@ enum {
   MOE_TAP_ALIGN_SCRATCH,    /* int32 scratch of the sort-and-pad stage */
   MOE_TAP_Y_SLICES,         /* float32 [S, T*top_k, roundup(H, 256)] K-slice partials of the
                                expert output per pair, summed in slice order by the combine;
-                               S > 1 only for decode shapes whose weight tiles in use would
-                               leave CUs idle (block_m <= 64), else empty */
+                               S > 1 only for decode shapes (block_m <= 64) whose weight
+                               tiles in use would leave CUs idle, else empty */
   MOE_TAP_COUNT
 };
 

@@ -89,13 +89,13 @@ def test_workspace_layout_is_disjoint_and_aligned():
 
 
 # K slices of the decode GEMM2: the weight tiles in use (one block per expert
-# plus ceil(P / block_m), times ceil(H / 256)) are raised to 1024 workgroups
+# plus ceil(P / block_m), times ceil(H / 256)) are raised to 2048 workgroups
 expect_slices = {(16, 256, 512, 8, 2): 4,            # 10 tiles: capped by I / 128 = 4
                  (64, 7168, 2048, 256, 8): 0,        # 288 blocks x 28 tiles: no split
                  (8192, 7168, 2048, 256, 8): 0,      # block_m 128: no split
                  (1, 2048, 768, 128, 8): 6,          # 9 blocks x 8 tiles: capped by I / 128 = 6
                  (512, 4096, 14336, 8, 2): 0,        # block_m 128
-                 (64, 4096, 14336, 8, 2): 6}         # 12 blocks x 16 tiles -> ceil(1024 / 192)
+                 (64, 4096, 14336, 8, 2): 8}         # 12 blocks x 16 tiles: capped at 8
 
 
 def test_forward_argument_checks():
