@@ -39,7 +39,7 @@ int pick_block_m(int T, int E, int top_k) {
 
 // K slices of the decode GEMM2 (block_m <= 64): when the weight tiles in use
 // (at most one block per expert plus ceil(P / block_m) more, times ceil(H / 256)
-// tiles of output features) would not give every CU of a 256-CU part eight
+// tiles of output features) would not give every CU of a 256-CU part four
 // workgroups, each tile's K is split over up to 8 workgroups (at most one per
 // 128-wide K block) that store float32 partials.  A function of the shape
 // alone, so the workspace size is known before anything runs.  (The same
@@ -51,7 +51,7 @@ int pick_kslices(int T, int H, int I, int E, int top_k, int BM) {
   const long long cap_blocks = (P + (long long)E * (BM - 1) + BM - 1) / BM;
   long long live = (P + BM - 1) / BM + (E < P ? E : P);
   if (live > cap_blocks) live = cap_blocks;
-  const long long tiles = live * ((H + 255) / 256), want = 8 * 256;
+  const long long tiles = live * ((H + 255) / 256), want = 4 * 256;
   if (tiles >= want) return 1;
   long long s = (want + tiles - 1) / tiles;
   if (s > 8) s = 8;

@@ -67,7 +67,8 @@ def test_block_m_choices():
 
 def test_workspace_layout_is_disjoint_and_aligned():
     for shape in [(16, 256, 512, 8, 2), (64, 7168, 2048, 256, 8), (8192, 7168, 2048, 256, 8),
-                  (1, 2048, 768, 128, 8), (512, 4096, 14336, 8, 2), (64, 4096, 14336, 8, 2)]:
+                  (1, 2048, 768, 128, 8), (512, 4096, 14336, 8, 2), (64, 4096, 14336, 8, 2),
+                  (32, 2048, 768, 128, 8)]:
         T, H, I, E, k = shape
         off = moe.moe_fp8_workspace_layout(*shape)
         total = moe.moe_fp8_workspace_bytes(*shape)
@@ -89,13 +90,14 @@ def test_workspace_layout_is_disjoint_and_aligned():
 
 
 # K slices of the decode GEMM2: the weight tiles in use (one block per expert
-# plus ceil(P / block_m), times ceil(H / 256)) are raised to 2048 workgroups
+# plus ceil(P / block_m), times ceil(H / 256)) are raised to 1024 workgroups
 expect_slices = {(16, 256, 512, 8, 2): 4,            # 10 tiles: capped by I / 128 = 4
                  (64, 7168, 2048, 256, 8): 0,        # 288 blocks x 28 tiles: no split
                  (8192, 7168, 2048, 256, 8): 0,      # block_m 128: no split
                  (1, 2048, 768, 128, 8): 6,          # 9 blocks x 8 tiles: capped by I / 128 = 6
                  (512, 4096, 14336, 8, 2): 0,        # block_m 128
-                 (64, 4096, 14336, 8, 2): 8}         # 12 blocks x 16 tiles: capped at 8
+                 (64, 4096, 14336, 8, 2): 6,         # 12 blocks x 16 tiles -> ceil(1024 / 192)
+                 (32, 2048, 768, 128, 8): 0}         # 136 blocks x 8 tiles >= 1024: no split
 
 
 def test_forward_argument_checks():
