@@ -18,7 +18,7 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIAS"}
 TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "pair_pos", "xq", "xs",
-        "aq", "as", "y", "align_scratch", "y_slices"]
+        "aq", "as", "y", "align_scratch", "y_slices", "h_slices"]
 MAX_EXPERTS = 512
 MAX_TOKENS = 16384
 MAX_TOP_K = 32
@@ -213,9 +213,11 @@ def workspace_taps(workspace, T, H, I, E, top_k, mx=False):
     cap = -(-(P + E * (bm - 1)) // bm) * bm
     ys = -(-H // 256) * 256
     total = (moe_fp8_mx_workspace_bytes if mx else moe_fp8_workspace_bytes)(T, H, I, E, top_k)
-    nslices = (total - off["y_slices"]) // (4 * P * ys)   # the last region: K-slice partials
-    if workspace.numel() < off["y_slices"] + 4 * P * ys * nslices:
-        nslices = 0          # a batched-format workspace: no K-slice region
+    # the two last regions: the GEMMs' K-slice partials (empty without slices)
+    nslices = (off["h_slices"] - off["y_slices"]) // (4 * P * ys)
+    nslices1 = (total - off["h_slices"]) // (8 * P * 2 * I)
+    if workspace.numel() < total:
+        nslices = nslices1 = 0          # a batched-format workspace: no K-slice regions
 
     def view(name, dtype, shape):
         n = 1
@@ -238,6 +240,7 @@ def workspace_taps(workspace, T, H, I, E, top_k, mx=False):
         "as": view("as", torch.uint8, (cap, I // 32)) if mx else view("as", torch.float32, (cap, I // 128)),
         "y": view("y", torch.bfloat16, (cap, -(-H // 256) * 256)),
         "y_slices": (view("y_slices", torch.float32, (nslices, P, ys)) if nslices > 1 else None),
+        "h_slices": (view("h_slices", torch.float64, (nslices1, P, 2 * I)) if nslices1 > 1 else None),
     }
 
 

@@ -76,6 +76,7 @@ struct GemmArgs {
   uint16_t* y_dump;          // GEMM2: 1024 bytes
   int ksplit;                // GEMM2 prefill: K slices per tile (1: bf16 y_out)
   float* part;               // GEMM2, ksplit > 1: float32 partials [ksplit, y_rows, y_stride]
+  double* h_slices;          // GEMM1 decode with K slices: float64 partials of h [slices, P, 2I]
   int mx;                    // GEMM2 prefill: act_scale and w_scale hold UE8M0 exponent bytes,
                              // one per row and 32 K elements ([rows, K/32] and [E, N, K/32])
 };
@@ -333,8 +334,15 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
 // are staged in LDS already converted to f16 (RM x 128 x 2 bytes, XOR
 // swizzled on 16-byte chunks, double buffered); weight fragments stream
 // from HBM into registers one K block ahead and are converted there.
-template <int RM>
-__global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, int split) {
+//
+// kSlices (decode shapes whose tiles in use would leave CUs idle): the
+// kslices workgroups of a tile each reduce one contiguous range of K blocks
+// and store their float64 partials of h by pair, h_slices[slice][p][0, 2I);
+// gemm1_slices_finish_kernel sums them in slice order and applies SiLU*mul
+// and the requant exactly as the epilogue below does.
+template <int RM, bool kSlices>
+__global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, int split,
+                                                        int kslices) {
   constexpr int NQ = RM / 16;
   constexpr int CHUNKS = RM * 8;               // 16-byte fp8 chunks of a token tile
   constexpr int CPT = (CHUNKS + 255) / 256;
@@ -345,22 +353,28 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
   const int g = lane >> 4, l16 = lane & 15;
   const TileCoord tc = tile_of(blockIdx.x, args);
   if (!tc.valid) return;
-  const int b = tc.b, half = tc.half, j = tc.j;
+  const int b = tc.b, j = tc.j;
+  // tc.half runs over the row parts of the block (split) times the K slices
+  const int half = kSlices ? tc.half / kslices : tc.half;
+  const int ks = kSlices ? tc.half - half * kslices : 0;
   const int row0 = b * BM + half * RM;
   if (split > 1 && load_uniform(args.sorted_ids + row0) >= args.P) return;   // padding only
   const int e = load_uniform(args.expert_ids + b);
-  const int K = args.K, nkb = K >> 7;
+  const int K = args.K, nkb_all = K >> 7;
+  // this workgroup's K blocks [kb0, kb0 + nkb)
+  const int kb0 = kSlices ? (int)((long long)ks * nkb_all / kslices) : 0;
+  const int nkb = kSlices ? (int)((long long)(ks + 1) * nkb_all / kslices) - kb0 : nkb_all;
 
   int prow[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) prow[pp] = (pp < 2 ? 0 : args.I) + 128 * j + 32 * wave + 16 * (pp & 1);
-  const uint8_t* wbase = args.w + (size_t)e * args.N * K;
+  const uint8_t* wbase = args.w + (size_t)e * args.N * K + (size_t)kb0 * 128;
   const uint8_t* wptr[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) wptr[pp] = wbase + (size_t)(prow[pp] + l16) * K + g * 16;
   const int nblk_n = args.N >> 7;
-  const float* ws0 = args.w_scale + ((size_t)e * nblk_n + j) * nkb;
-  const float* ws1 = args.w_scale + ((size_t)e * nblk_n + (args.I >> 7) + j) * nkb;
+  const float* ws0 = args.w_scale + ((size_t)e * nblk_n + j) * nkb_all + kb0;
+  const float* ws1 = args.w_scale + ((size_t)e * nblk_n + (args.I >> 7) + j) * nkb_all + kb0;
 
   const uint8_t* aptr[CPT];
   int soff0[CPT], soff1[CPT];
@@ -374,7 +388,7 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
       soff0[i] = r * 256 + (((2 * ch) ^ (r & 15)) << 4);
       soff1[i] = r * 256 + (((2 * ch + 1) ^ (r & 15)) << 4);
       const int p = args.sorted_ids[row0 + r];
-      if (p < args.P) aptr[i] = args.act + (size_t)(p / args.top_k) * K + ch * 16;
+      if (p < args.P) aptr[i] = args.act + (size_t)(p / args.top_k) * K + (size_t)kb0 * 128 + ch * 16;
     }
   }
   const float* sptr[NQ];
@@ -383,7 +397,7 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
   for (int q = 0; q < NQ; ++q) {
     const int rq = 16 * q + l16;
     const int p = args.sorted_ids[row0 + rq];
-    sptr[q] = p < args.P ? args.act_scale + (size_t)(p / args.top_k) * nkb : nullptr;
+    sptr[q] = p < args.P ? args.act_scale + (size_t)(p / args.top_k) * nkb_all + kb0 : nullptr;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int idx = 2 * g + (c & 1) + 8 * (c >> 1);
@@ -480,6 +494,25 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
     sw1 = sw1_n;
   }
 
+  if (kSlices) {
+    // float64 partials of the pair's gate and up features of this wave
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int p = args.sorted_ids[row0 + 16 * q + l16];
+      if (p >= args.P) continue;
+      double* hrow = args.h_slices + ((size_t)ks * args.P + p) * (2 * (size_t)args.I);
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        const int i = 128 * j + 32 * wave + 16 * pg + 4 * g;
+        *(double2*)(hrow + i) = make_double2(acc[pg][q][0], acc[pg][q][1]);
+        *(double2*)(hrow + i + 2) = make_double2(acc[pg][q][2], acc[pg][q][3]);
+        *(double2*)(hrow + args.I + i) = make_double2(acc[pg + 2][q][0], acc[pg + 2][q][1]);
+        *(double2*)(hrow + args.I + i + 2) = make_double2(acc[pg + 2][q][2], acc[pg + 2][q][3]);
+      }
+    }
+    return;
+  }
+
   // a = silu(gate) * up in float64, rounded once to float32, then requantised
   // per row over the 128 features of tile j
   float av[NQ][2][4];
@@ -520,6 +553,50 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
     }
     if (wave == 0 && lane < 16) args.as_out[grow * (Iq >> 7) + j] = s;
   }
+}
+
+// The end of moe_gemm1_kernel<RM, true>: per pair p (at sorted row pair_pos[p])
+// and 128-feature group j, h = the float64 sum of the slices' partials in
+// slice order, then a = float32(silu(gate) * up) evaluated in float64, the
+// group's amax, scale and e4m3 codes, exactly as that kernel's own epilogue.
+// Half a wave per (p, j): lane l holds features 128 j + 4 l .. 4 l + 3.
+__global__ __launch_bounds__(256) void gemm1_slices_finish_kernel(const double* __restrict__ hs,
+                                                                  int kslices, int P, int I,
+                                                                  const int32_t* __restrict__ pair_pos,
+                                                                  uint8_t* __restrict__ aq,
+                                                                  float* __restrict__ as) {
+  const int nj = I >> 7;
+  const long long hw = ((long long)blockIdx.x * 256 + threadIdx.x) >> 5;   // half-wave index
+  const int l = threadIdx.x & 31;
+  const bool on = hw < (long long)P * nj;
+  const int p = on ? (int)(hw / nj) : 0, j = on ? (int)(hw - (long long)p * nj) : 0;
+  const int row = on ? pair_pos[p] : -1;
+  const int i = 128 * j + 4 * l;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  float m = 0.0f;
+  if (row >= 0) {
+    double gt[4] = {0.0, 0.0, 0.0, 0.0}, up[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int s = 0; s < kslices; ++s) {
+      const double* h = hs + ((size_t)s * P + p) * (2 * (size_t)I);
+      const double2 g0 = *(const double2*)(h + i), g1 = *(const double2*)(h + i + 2);
+      const double2 u0 = *(const double2*)(h + I + i), u1 = *(const double2*)(h + I + i + 2);
+      gt[0] += g0.x; gt[1] += g0.y; gt[2] += g1.x; gt[3] += g1.y;
+      up[0] += u0.x; up[1] += u0.y; up[2] += u1.x; up[3] += u1.y;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a[r] = (float)(gt[r] / (1.0 + exp(-gt[r])) * up[r]);
+      m = __builtin_fmaxf(m, __builtin_fabsf(a[r]));
+    }
+  }
+  m = wave_max_xor(m, 16, 1);             // within the half-wave
+  if (row < 0) return;
+  float s, rcp;
+  group_scale(m, s, rcp);
+  *(uint32_t*)(aq + (size_t)row * I + i) =
+      pack4_e4m3(clamp_fp8(div_by_scale(a[0], s, rcp)), clamp_fp8(div_by_scale(a[1], s, rcp)),
+                 clamp_fp8(div_by_scale(a[2], s, rcp)), clamp_fp8(div_by_scale(a[3], s, rcp)));
+  if (l == 0) as[(size_t)row * nj + j] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -1577,7 +1654,10 @@ static hipError_t launch_gemm2_bm(const GemmArgs& a, int BM, hipStream_t stream)
 hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, const float* w13s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
-                        uint8_t* aq, float* as, hipStream_t stream) {
+                        uint8_t* aq, float* as, int kslices, double* h_slices,
+                        const int32_t* pair_pos, hipStream_t stream) {
+  if (kslices > 1 && (BM > 64 || !h_slices || !pair_pos || kslices > (H >> 7)))
+    return hipErrorInvalidValue;
   GemmArgs a{};
   a.eoff = eoff; a.E = E;
   a.act = xq; a.act_scale = xs; a.w = w13; a.w_scale = w13s;
@@ -1593,12 +1673,29 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
   }
   const int rm = BM < 32 ? BM : 32;
   const int split = BM / rm;
+  if (kslices > 1) {
+    a.split = split * kslices;
+    a.h_slices = h_slices;
+    const dim3 grid((unsigned)(nblk * a.split * a.n_tiles)), block(256);
+    if (rm == 16)
+      hipLaunchKernelGGL((moe_gemm1_kernel<16, true>), grid, block, 0, stream, a, BM, split, kslices);
+    else if (rm == 32)
+      hipLaunchKernelGGL((moe_gemm1_kernel<32, true>), grid, block, 0, stream, a, BM, split, kslices);
+    else
+      return hipErrorInvalidValue;
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const long long threads = (long long)P * (I >> 7) * 32;
+    hipLaunchKernelGGL(gemm1_slices_finish_kernel, dim3((unsigned)((threads + 255) / 256)), block, 0,
+                       stream, h_slices, kslices, P, I, pair_pos, aq, as);
+    return hipGetLastError();
+  }
   a.split = split;
   const dim3 grid((unsigned)(nblk * split * a.n_tiles)), block(256);
   if (rm == 16)
-    hipLaunchKernelGGL(moe_gemm1_kernel<16>, grid, block, 0, stream, a, BM, split);
+    hipLaunchKernelGGL((moe_gemm1_kernel<16, false>), grid, block, 0, stream, a, BM, split, 1);
   else if (rm == 32)
-    hipLaunchKernelGGL(moe_gemm1_kernel<32>, grid, block, 0, stream, a, BM, split);
+    hipLaunchKernelGGL((moe_gemm1_kernel<32, false>), grid, block, 0, stream, a, BM, split, 1);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -28,10 +28,16 @@ hipError_t launch_align(const int32_t* ids, const int32_t* emap, int n_map, int 
 hipError_t launch_identity_layout(int M, int BM, int nblk, int32_t* sorted_ids,
                                   int32_t* expert_ids, int32_t* eoff, int32_t* ntpp,
                                   hipStream_t stream);
+// kslices > 1 (block_m <= 64, at most H/128 slices): the workgroups of a tile
+// split K and store float64 partials of h by pair, h_slices [kslices, P, 2I];
+// a second kernel sums them and writes aq / as at each pair's sorted row
+// (pair_pos; padding rows of aq are then left unwritten, and nothing reads
+// their results)
 hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, const float* w13s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
-                        uint8_t* aq, float* as, hipStream_t stream);
+                        uint8_t* aq, float* as, int kslices, double* h_slices,
+                        const int32_t* pair_pos, hipStream_t stream);
 // kslices > 1 (block_m <= 64, at most I/128 slices): the workgroups of a tile
 // split K and store float32 partials by pair, y_slices [kslices, P, y_stride],
 // for launch_combine_slices; otherwise bf16 y by sorted row

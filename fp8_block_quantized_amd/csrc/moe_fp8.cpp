@@ -59,8 +59,30 @@ int pick_kslices(int T, int H, int I, int E, int top_k, int BM) {
   return (int)s;
 }
 
+// K slices of the decode GEMM1 (block_m <= 64), by the same rule over its
+// tiles (blocks in use x the block's row parts x I/128 feature groups) with
+// a target of two workgroups per CU; at most 8 slices and one per 128-wide
+// K block of H.  The slices' float64 partials are summed before SiLU*mul by
+// a second kernel, whose launch and partial traffic cost more than a third
+// workgroup per CU gains (the Qwen3-shaped T=32 ran slower split in two).
+int pick_kslices1(int T, int H, int I, int E, int top_k, int BM) {
+  if (BM > 64) return 1;
+  const long long P = (long long)T * top_k;
+  const long long cap_blocks = (P + (long long)E * (BM - 1) + BM - 1) / BM;
+  long long live = (P + BM - 1) / BM + (E < P ? E : P);
+  if (live > cap_blocks) live = cap_blocks;
+  const long long rows_split = BM / (BM < 32 ? BM : 32);
+  const long long tiles = live * rows_split * (I / 128), want = 2 * 256;
+  if (tiles >= want) return 1;
+  long long s = (want + tiles - 1) / tiles;
+  if (s > 8) s = 8;
+  if (s > H / 128) s = H / 128;
+  return (int)s;
+}
+
 struct Layout {
   int BM;
+  int kslices1;      // K slices of GEMM1 (1: its own epilogue requantises)
   int kslices;       // K slices of GEMM2 (1: bf16 y by sorted row)
   size_t cap;
   size_t off[MOE_TAP_COUNT];
@@ -76,6 +98,7 @@ void make_layout(int T, int H, int I, int E, int top_k, Layout& L, int block_m =
   const size_t P = (size_t)T * top_k;
   L.BM = block_m ? block_m : pick_block_m(T, E, top_k);
   L.kslices = slices ? pick_kslices(T, H, I, E, top_k, L.BM) : 1;
+  L.kslices1 = slices ? pick_kslices1(T, H, I, E, top_k, L.BM) : 1;
   L.cap = round_up(P + (size_t)E * (L.BM - 1), L.BM);
   size_t sz[MOE_TAP_COUNT];
   sz[MOE_TAP_TOPK_IDS] = P * 4;
@@ -91,6 +114,7 @@ void make_layout(int T, int H, int I, int E, int top_k, Layout& L, int block_m =
   sz[MOE_TAP_Y] = L.cap * y_stride(H) * 2;
   sz[MOE_TAP_ALIGN_SCRATCH] = moe::align_scratch_bytes((int)P, E);
   sz[MOE_TAP_Y_SLICES] = L.kslices > 1 ? (size_t)L.kslices * P * y_stride(H) * 4 : 0;
+  sz[MOE_TAP_H_SLICES] = L.kslices1 > 1 ? (size_t)L.kslices1 * P * 2 * I * 8 : 0;
   size_t o = 0;
   for (int i = 0; i < MOE_TAP_COUNT; ++i) {
     L.off[i] = o;
@@ -280,8 +304,9 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
   if ((err = moe::launch_group_quant(x, T, H, xq, xs, stream))) return MOE_ERR_HIP;
   if (mark(3)) return MOE_ERR_HIP;
   const int32_t* eoff = moe::align_expert_offsets(scratch, P, EL);
+  double* hslices = (double*)(ws + L.off[MOE_TAP_H_SLICES]);
   if ((err = moe::launch_gemm1(xq, xs, w13, w13_scale, sorted, eids, ntpp, eoff, EL, H, I, P,
-                               top_k, L.BM, nblk, aq, as, stream)))
+                               top_k, L.BM, nblk, aq, as, L.kslices1, hslices, ppos, stream)))
     return MOE_ERR_HIP;
   if (mark(4)) return MOE_ERR_HIP;
   float* yslices = (float*)(ws + L.off[MOE_TAP_Y_SLICES]);
@@ -392,7 +417,7 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, con
   if (moe::launch_group_quant_masked(x, expert_num_tokens, E, max_tokens, H, xq, xs, stream))
     return MOE_ERR_HIP;
   if (moe::launch_gemm1(xq, xs, w13, w13_scale, sorted, eids, ntpp, eoff, E, H, I, T, 1, L.BM,
-                        nblk, aq, as, stream))
+                        nblk, aq, as, 1, nullptr, nullptr, stream))
     return MOE_ERR_HIP;
   if (moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, T, L.BM, nblk, y,
                         (int)y_stride(H), 1, nullptr, stream))

@@ -86,6 +86,10 @@ enum {
                                expert output per pair, summed in slice order by the combine;
                                S > 1 only for decode shapes (block_m <= 64) whose weight
                                tiles in use would leave CUs idle, else empty */
+  MOE_TAP_H_SLICES,         /* float64 [S1, T*top_k, 2I] K-slice partials of the first GEMM's
+                               gate and up outputs per pair, summed in slice order before
+                               SiLU*mul; S1 > 1 under the same condition, else empty (with
+                               S1 > 1, MOE_TAP_AQ / MOE_TAP_AS rows of padding are unwritten) */
   MOE_TAP_COUNT
 };
 

@@ -77,27 +77,33 @@ def test_workspace_layout_is_disjoint_and_aligned():
         cap = -(-(P + E * (bm - 1)) // bm) * bm
         size = {"topk_ids": 4 * P, "topk_weights": 4 * P, "sorted_ids": 4 * cap,
                 "expert_ids": 4 * (cap // bm), "ntpp": 4, "pair_pos": 4 * P, "xq": T * H, "xs": 4 * T * H // 128,
-                "aq": cap * I, "as": 4 * cap * I // 128, "y": 2 * cap * (-(-H // 256) * 256), "align_scratch": 0}
+                "aq": cap * I, "as": 4 * cap * I // 128, "y": 2 * cap * (-(-H // 256) * 256), "align_scratch": 0,
+                "y_slices": 0}
         names = moe.TAPS
         for a, b in zip(names, names[1:]):
             assert off[a] % 256 == 0
             assert off[a] + size[a] <= off[b]
-        # the last region holds the second GEMM's K-slice partials, or nothing
+        # the two last regions hold the GEMMs' K-slice partials, or nothing
         ys = -(-H // 256) * 256
-        slices = (total - off["y_slices"]) // (4 * P * ys)
-        assert off["y_slices"] % 256 == 0 and off["y_slices"] + 4 * P * ys * slices <= total
-        assert slices == expect_slices[shape]
+        slices2 = (off["h_slices"] - off["y_slices"]) // (4 * P * ys)
+        slices1 = (total - off["h_slices"]) // (8 * P * 2 * I)
+        assert off["y_slices"] + 4 * P * ys * slices2 <= off["h_slices"]
+        assert off["h_slices"] % 256 == 0 and off["h_slices"] + 8 * P * 2 * I * slices1 <= total
+        assert (slices1, slices2) == expect_slices[shape]
 
 
-# K slices of the decode GEMM2: the weight tiles in use (one block per expert
-# plus ceil(P / block_m), times ceil(H / 256)) are raised to 1024 workgroups
-expect_slices = {(16, 256, 512, 8, 2): 4,            # 10 tiles: capped by I / 128 = 4
-                 (64, 7168, 2048, 256, 8): 0,        # 288 blocks x 28 tiles: no split
-                 (8192, 7168, 2048, 256, 8): 0,      # block_m 128: no split
-                 (1, 2048, 768, 128, 8): 6,          # 9 blocks x 8 tiles: capped by I / 128 = 6
-                 (512, 4096, 14336, 8, 2): 0,        # block_m 128
-                 (64, 4096, 14336, 8, 2): 6,         # 12 blocks x 16 tiles -> ceil(1024 / 192)
-                 (32, 2048, 768, 128, 8): 0}         # 136 blocks x 8 tiles >= 1024: no split
+# K slices (GEMM1, GEMM2) of the decode GEMMs (0: none).  The tiles in use
+# (blocks: one per expert plus ceil(P / block_m), at most the capacity;
+# GEMM1 times I / 128 feature groups, GEMM2 times ceil(H / 256) feature
+# tiles) are raised towards 512 (GEMM1) and 1024 (GEMM2) workgroups, at most
+# 8 slices and one per 128-wide K block.
+expect_slices = {(16, 256, 512, 8, 2): (2, 4),       # 10 blocks: capped by H / 128, I / 128
+                 (64, 7168, 2048, 256, 8): (0, 0),   # 272 blocks x 16 groups, x 28 tiles
+                 (8192, 7168, 2048, 256, 8): (0, 0), # block_m 128
+                 (1, 2048, 768, 128, 8): (8, 6),     # 9 blocks: 54 groups, 72 tiles
+                 (512, 4096, 14336, 8, 2): (0, 0),   # block_m 128
+                 (64, 4096, 14336, 8, 2): (0, 6),    # 12 blocks: 1344 groups; 192 tiles
+                 (32, 2048, 768, 128, 8): (0, 0)}    # 136 blocks: 816 groups; 1088 tiles
 
 
 def test_forward_argument_checks():

@@ -186,21 +186,26 @@ def test_full_size_workloads(name, T):
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [
-    (37, 256, 384, 4, 4),     # block_m 64, 7 tiles in use at most: 3 slices (I / 128)
-    (3, 512, 512, 64, 8),     # block_m 16, 26 blocks x 2 tiles: 4 slices
+    (37, 256, 384, 4, 4),     # block_m 64: GEMM1 2 slices (H / 128), GEMM2 3 (I / 128)
+    (3, 512, 512, 64, 8),     # block_m 16, 26 blocks: GEMM1 4 slices, GEMM2 4
 ])
 def test_k_slice_partials(T, H, I, E, k):
-    """Decode shapes whose weight tiles would leave CUs idle split GEMM2's K:
-    the float32 partials, summed over the slices, are the per-pair expert
-    output y of the oracle (before the routing weight)."""
+    """Decode shapes whose weight tiles would leave CUs idle split both GEMMs'
+    K.  GEMM1's float64 partials, summed over the slices, give the oracle's
+    SiLU*mul activation a; GEMM2's float32 partials, summed, the per-pair
+    expert output y (before the routing weight)."""
     w = _layer(T, H, I, E, k, seed=3 * T + E)
     g = to_dev(w)
     note(f"forward K slices T={T} H={H} I={I} E={E} k={k}")
     out, taps, _ = _run(g, T, H, I, E, k, True)
+    assert taps["h_slices"] is not None and taps["h_slices"].shape[0] > 1
     assert taps["y_slices"] is not None and taps["y_slices"].shape[0] > 1
     ref, info = ref_moe.moe_forward(w["x"].float().numpy(), w["logits"].numpy(), w["w13"].numpy(),
                                     w["w13_scale"].numpy(), w["w2"].numpy(), w["w2_scale"].numpy(),
                                     k, True)
+    h = np_(taps["h_slices"]).sum(axis=0)
+    a = (ref_moe.silu(h[:, :I]) * h[:, I:]).astype(np.float32)
+    np.testing.assert_allclose(a, info["a"], rtol=1e-5, atol=1e-6)
     y = np_(taps["y_slices"]).astype(np.float64).sum(axis=0)[:, :H]
     assert_out_close(y, info["y"], "summed K-slice partials")
     assert_out_close(np_(out.float()), ref, "output")
