@@ -128,6 +128,80 @@ __global__ __launch_bounds__(1024) void align_scatter_kernel(
   }
 }
 
+// The three steps in one workgroup, for at most kChunk pairs (decode
+// batches): the histogram, the padded offsets and the ranks stay in LDS, and
+// only the expert block offsets go to the scratch for the GEMMs.  The same
+// layout as count + scan + scatter, from one launch instead of three.
+__global__ __launch_bounds__(1024) void align_single_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ emap, int n_map, int P, int E,
+    int BM, int ebits, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ ntpp, int32_t* __restrict__ eoff, int32_t* __restrict__ pair_pos) {
+  __shared__ int hist[kMaxE];
+  __shared__ int scan[kChunk];
+  __shared__ int wcnt[kChunk / 64][kMaxE];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int e = t; e < E; e += kChunk) hist[e] = 0;
+  for (int i = t; i < (kChunk / 64) * E; i += kChunk) wcnt[i / E][i % E] = 0;
+  __syncthreads();
+  // 1. per-expert counts
+  const int p = t;
+  const int e0 = p < P ? pair_expert(ids, emap, n_map, p) : -1;
+  const bool valid = (unsigned)e0 < (unsigned)E;
+  if (valid) atomicAdd(&hist[e0], 1);
+  __syncthreads();
+  // 2. padded offsets, sentinels, block -> expert table
+  const int total = t < E ? hist[t] : 0;
+  const int pad = (total + BM - 1) / BM * BM;
+  scan[t] = pad;
+  __syncthreads();
+  for (int off = 1; off < kChunk; off <<= 1) {
+    const int v = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  const int excl = scan[t] - pad;
+  const int padded_total = scan[kChunk - 1];
+  if (t == 0) {
+    ntpp[0] = padded_total;
+    eoff[E] = padded_total / BM;
+  }
+  if (t < E) {
+    eoff[t] = excl / BM;
+    hist[t] = excl;                        // from here on: the expert's first row
+    for (int r = total; r < pad; ++r) sorted_ids[excl + r] = P;
+  }
+  const int nblocks = padded_total / BM;
+  for (int blk = t; blk < nblocks; blk += kChunk) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (scan[mid] > blk * BM) hi = mid; else lo = mid + 1;
+    }
+    expert_ids[blk] = lo;
+  }
+  // 3. stable ranks: ballot match inside each wave, counts of earlier waves
+  const int e = valid ? e0 : 0;
+  unsigned long long peers = __ballot(valid);
+  for (int bit = 0; bit < ebits; ++bit) {
+    const bool b = (e >> bit) & 1;
+    const unsigned long long m = __ballot(b);
+    peers &= b ? m : ~m;
+  }
+  const int rank_in_wave = __popcll(peers & ((1ull << lane) - 1ull));
+  if (valid && rank_in_wave == 0) wcnt[wave][e] = __popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wcnt[w][e];
+    const int pos = hist[e] + before + rank_in_wave;
+    sorted_ids[pos] = p;
+    if (pair_pos) pair_pos[p] = pos;
+  } else if (pair_pos && p < P) {
+    pair_pos[p] = -1;
+  }
+}
+
 // The layout of one expert owning every row (the dense linear): sorted row r
 // holds row r of the input (the sentinel M past its end), every block belongs
 // to expert 0, eoff = {0, nblk} and the padded row count is nblk * BM.
@@ -243,6 +317,11 @@ hipError_t launch_align(const int32_t* ids, const int32_t* emap, int n_map, int 
   int32_t* eoff = base + (size_t)nchunk * E;
   int ebits = 0;
   while ((1 << ebits) < E) ++ebits;
+  if (nchunk == 1) {
+    hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(kChunk), 0, stream, ids, emap, n_map, P,
+                       E, BM, ebits, sorted_ids, expert_ids, ntpp, eoff, pair_pos);
+    return hipGetLastError();
+  }
   if (nchunk > 0)
     hipLaunchKernelGGL(align_count_kernel, dim3(nchunk), dim3(kChunk), 0, stream, ids, emap, n_map,
                        P, E, counts);
