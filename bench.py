@@ -39,12 +39,12 @@ STAGE_PEAK = {"gemm1": MFMA_F16_PEAK, "gemm2": MFMA_FP8_PEAK}
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
 # kernel source they were taken on: bench reports null traffic once
 # gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "cb59f7c100b10a87884f98b9e52e48279c8ed1384236e6450fd245ae7682af95"
+TRAFFIC_SOURCE_SHA256 = "c57127a888b3849badba0b4dbc0ef443f82969b6c542f60ea5be158607bd4216"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
-    "prefill.gemm1": (10746841842, 184494741),
-    "prefill.gemm2": (4406276364, 1208267456),
-    "decode.gemm1": (4795529278, 5720939),
-    "decode.gemm2": (2408703763, 7340224),
+    "prefill.gemm1": (10748266557, 184470912),
+    "prefill.gemm2": (4397065067, 1208267115),
+    "decode.gemm1": (4795674564, 5724203),
+    "decode.gemm2": (2408673012, 7340288),
 }
 
 
