@@ -56,8 +56,10 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
   __shared__ int scan[kChunk];
   const int e = threadIdx.x;
   int total = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int b = 0; b < nchunk; ++b) total += counts[(size_t)b * E + e];
+  }
   const int pad = (total + BM - 1) / BM * BM;
   scan[e] = pad;
   __syncthreads();
@@ -76,6 +78,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
   if (e == 0) eoff[E] = padded_total / BM;
   if (e < E) {
     int run = excl;
+#pragma unroll 8
     for (int b = 0; b < nchunk; ++b) {
       base[(size_t)b * E + e] = run;
       run += counts[(size_t)b * E + e];
