@@ -366,12 +366,38 @@ def main():
             mx_layer[n] = r
             del mws
         del mxw
-        return quant, dense, dense_mx, batched, mx_layer
+        # what this part sustains: a plain 1 GiB device copy (read + write) and
+        # register-only MFMA chains of the two GEMMs' instruction types
+        nb = 1 << 30
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        copy_ms = []
+        for _ in range(5):
+            ce[0].record()
+            dst.copy_(src)
+            ce[1].record()
+            torch.cuda.synchronize()
+            copy_ms.append(ce[0].elapsed_time(ce[1]))
+        del src, dst
+        nblk = 2048
+        sink = torch.empty(nblk * 256, dtype=torch.float32, device=dev)
+        peaks = {"hbm_copy_GB_per_s": 2 * nb / (min(copy_ms) * 1e-3) / 1e9}
+        for kind, iters in (("f16", 5000), ("fp8", 2500)):
+            moe.moe_mfma_rate_probe(kind, 100, nblk, sink)
+            torch.cuda.synchronize()
+            ce[0].record()
+            fl = moe.moe_mfma_rate_probe(kind, iters, nblk, sink)
+            ce[1].record()
+            torch.cuda.synchronize()
+            peaks[f"mfma_{kind}_TFLOP_per_s"] = fl / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e12
+        del sink
+        return quant, dense, dense_mx, batched, mx_layer, peaks
 
     if args.layer_only:
-        quant = dense = dense_mx = batched = mx_layer = None
+        quant = dense = dense_mx = batched = mx_layer = peaks = None
     else:
-        quant, dense, dense_mx, batched, mx_layer = extras()
+        quant, dense, dense_mx, batched, mx_layer, peaks = extras()
 
     dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
     dom = kernels[dom_name]
@@ -382,6 +408,11 @@ def main():
         same_source = hashlib.sha256(fh.read()).hexdigest() == TRAFFIC_SOURCE_SHA256
     if args.workload == "dsv3" and same_source and dom_name in TRAFFIC:
         traffic = float(sum(TRAFFIC[dom_name]))
+    if peaks:
+        key = {"GB/s": "hbm_copy_GB_per_s"}.get(roof["unit"],
+                                              "mfma_f16_TFLOP_per_s" if dom["peak"] == MFMA_F16_PEAK
+                                              else "mfma_fp8_TFLOP_per_s")
+        roof["frac_of_measured_peak"] = roof["achieved"] / peaks[key]
     roof.update({"kernel": dom_name, "traffic": traffic, "traffic_unit": "bytes per launch",
                  "alg_bytes_per_launch": dom["bytes"], "alg_flops_per_launch": dom["flops"],
                  "ms_per_launch": dom["ms"]})
@@ -406,6 +437,7 @@ def main():
         "dense_linear_mxfp8": dense_mx,
         "batched_experts": batched,
         "moe_mxfp8": mx_layer,
+        "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline and "decode" in phases:
         ph = phases["decode"]

@@ -33,7 +33,7 @@ EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layo
            "moe_fp8_mx_workspace_bytes", "moe_fp8_mx_workspace_layout", "moe_fp8_mx_forward",
            "moe_align_scratch_bytes", "moe_align", "moe_status_string",
            "fp8_block_linear_workspace_bytes", "fp8_block_linear",
-           "mxfp8_linear_workspace_bytes", "mxfp8_linear"]
+           "mxfp8_linear_workspace_bytes", "mxfp8_linear", "moe_mfma_rate_probe"]
 
 
 class MoeError(RuntimeError):
@@ -99,6 +99,8 @@ def load_library(path=LIB_PATH):
     lib.mxfp8_linear.restype = c_int
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_mfma_rate_probe.argtypes = [c_int, c_int, c_int, vp, vp]
+    lib.moe_mfma_rate_probe.restype = c_int
     _lib = lib
     return lib
 
@@ -432,3 +434,20 @@ def moe_fp8_mx_forward(x, router_logits, w13, w13_scale, w2, w2_scale, top_k, re
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check("moe_fp8_mx_forward", st)
     return out
+
+
+MFMA_PROBE_FLOPS = {"f16": 16384, "fp8": 65536}    # per instruction
+
+
+def moe_mfma_rate_probe(kind, iters, nblocks, sink, stream=None):
+    """Matrix-core rate probe ("f16": the first GEMM's v_mfma_f32_16x16x32_f16,
+    "fp8": the second GEMM's FP8 16x16x128): nblocks x 4 waves x iters x 8
+    MFMAs from registers; sink is a float32 device tensor of nblocks * 256.
+    Returns the flops the launch performs."""
+    k = {"f16": 0, "fp8": 1}[kind]
+    if sink.numel() < nblocks * 256:
+        raise ValueError("sink needs nblocks * 256 floats")
+    st = load_library().moe_mfma_rate_probe(k, int(iters), int(nblocks),
+                                            _dev(sink, torch.float32, "sink"), _stream(stream))
+    _check("moe_mfma_rate_probe", st)
+    return nblocks * 4 * iters * 8 * MFMA_PROBE_FLOPS[kind]

@@ -11,12 +11,18 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_fp8.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_fp8.cpp", "quant.hip", "router.hip", "align.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["moe_fp8.cpp", "quant.hip", "router.hip", "align.hip", "gemm.hip", "combine.hip",
+           "probe.hip"]
 
 # -ffp-contract=off: the arithmetic is exactly as written (explicit fmaf where
 # a fused multiply-add is wanted).  Packed fp32 VALU ops are disabled.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs; otherwise the
+# register allocator may park them in AGPRs and copy them back and forth
+# around every MFMA inside a loop (in the decode GEMMs, and in a register-only
+# MFMA loop, where the copies halved the f16 rate).
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wno-unused-command-line-argument"]
 
 

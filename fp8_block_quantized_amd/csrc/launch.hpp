@@ -85,4 +85,8 @@ hipError_t launch_combine_slices(const float* part, int y_stride, int nslice, in
                                  const int32_t* pair_pos, const float* topk_w, int T, int H,
                                  int top_k, uint16_t* out, hipStream_t stream);
 
+// matrix-core rate probe (kind 0: f16 16x16x32, 1: FP8 16x16x128), nblocks x 256
+// threads, one float per thread stored to sink
+hipError_t launch_mfma_probe(int kind, int iters, int nblocks, float* sink, hipStream_t stream);
+
 }  // namespace moe

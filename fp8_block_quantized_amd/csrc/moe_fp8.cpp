@@ -680,4 +680,12 @@ int mxfp8_linear(const void* x, const uint8_t* w, const uint8_t* w_scale, int M,
   return MOE_OK;
 }
 
+int moe_mfma_rate_probe(int kind, int iters, int nblocks, float* sink, hipStream_t stream) {
+  if (kind != 0 && kind != 1) return MOE_ERR_UNSUPPORTED;
+  if (iters < 1 || nblocks < 1 || nblocks > (1 << 20)) return MOE_ERR_SHAPE;
+  if (!sink) return MOE_ERR_NULL;
+  if ((uintptr_t)sink % 4) return MOE_ERR_UNSUPPORTED;
+  return moe::launch_mfma_probe(kind, iters, nblocks, sink, stream) ? MOE_ERR_HIP : MOE_OK;
+}
+
 }  // extern "C"

@@ -412,6 +412,24 @@ size_t mxfp8_linear_workspace_bytes(int M, int N, int K);
 int mxfp8_linear(const void* x, const uint8_t* w, const uint8_t* w_scale, int M, int N, int K,
                  void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Matrix-core rate probe, a measurement aid (not a step of the layer): the
+ * roofline fractions of the GEMMs are quoted against MI355X's published
+ * dense peaks, and this gives the rate the part actually sustains for the
+ * two MFMA types the GEMMs issue.  nblocks workgroups of 4 waves each run
+ * iters rounds of 8 independent accumulator chains of one instruction:
+ *   kind 0: v_mfma_f32_16x16x32_f16 (first GEMM), 16384 flops each;
+ *   kind 1: v_mfma_scale_f32_16x16x128_f8f6f4, e4m3 x e4m3 with unit scales
+ *           (second GEMM), 65536 flops each.
+ * So one call performs nblocks * 4 * iters * 8 instructions.  Operands live
+ * in registers; the only memory access is one float32 store per thread to
+ * sink [nblocks * 256] (device, 4-byte aligned, caller-owned; contents
+ * meaningless).  Returns MOE_OK, MOE_ERR_UNSUPPORTED for another kind,
+ * MOE_ERR_SHAPE unless iters >= 1 and 1 <= nblocks <= 2^20, MOE_ERR_NULL
+ * for a null sink, MOE_ERR_HIP if the launch fails.
+ */
+int moe_mfma_rate_probe(int kind, int iters, int nblocks, float* sink, hipStream_t stream);
+
 /* Static description of a moe_status code. */
 const char* moe_status_string(int status);
 

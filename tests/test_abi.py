@@ -290,3 +290,17 @@ def test_mx_forward_argument_checks():
     a = list(base); a[14] = n - 1; assert f(*a) == -4
     a = list(base); a[3] = vp(0x40002); assert f(*a) == -3   # exponents misaligned
     a = list(base); a[12] = vp(0x10000 + 64); assert f(*a) == -6   # out overlaps x
+
+
+def test_mfma_probe_argument_checks():
+    # every call below is invalid, so it returns before anything is launched
+    f = moe.load_library().moe_mfma_rate_probe
+    vp = ctypes.c_void_p
+    sink = vp(0x7000000000)
+    assert f(2, 10, 4, sink, None) == -3          # unknown instruction kind
+    assert f(0, 0, 4, sink, None) == -2           # no rounds
+    assert f(1, 10, 0, sink, None) == -2          # no workgroups
+    assert f(0, 10, (1 << 20) + 1, sink, None) == -2
+    assert f(0, 10, 4, None, None) == -1          # no sink
+    assert f(1, 10, 4, vp(0x7000000002), None) == -3   # misaligned sink
+    assert moe.MFMA_PROBE_FLOPS == {"f16": 16 * 16 * 32 * 2, "fp8": 16 * 16 * 128 * 2}
