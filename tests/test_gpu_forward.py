@@ -209,3 +209,32 @@ def test_k_slice_partials(T, H, I, E, k):
     y = np_(taps["y_slices"]).astype(np.float64).sum(axis=0)[:, :H]
     assert_out_close(y, info["y"], "summed K-slice partials")
     assert_out_close(np_(out.float()), ref, "output")
+
+
+def test_maximum_sizes():
+    """The largest call the ABI accepts in tokens, experts and top_k at once
+    (T = 16384, E = 512, top_k = 32: 524,288 pairs, 128-row blocks, 512 align
+    chunks), with small H and I.  Routing, layout and activation codes on
+    every token; the output on sampled tokens."""
+    T, H, I, E, k = moe.MAX_TOKENS, 256, 256, moe.MAX_EXPERTS, moe.MAX_TOP_K
+    w = _layer(T, H, I, E, k, seed=77)
+    g = to_dev(w)
+    note(f"forward maximum sizes T={T} H={H} I={I} E={E} k={k}")
+    out, taps, _ = _run(g, T, H, I, E, k, True)
+    from oracle import quant as ref_quant
+    from oracle import router as ref_router
+    logits_np = w["logits"].numpy()
+    rids, rw = ref_router.topk_softmax(logits_np, k, True)
+    rows = _check_taps(taps, {"ids": rids, "w": rw}, rids, E, "maximum sizes")
+    x_np = w["x"].float().numpy()
+    xq, xs = ref_quant.per_token_group_quant(x_np)
+    assert np.array_equal(np_(taps["xq"]), xq) and np.array_equal(np_(taps["xs"]), xs)
+    tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(5).choice(T, 6, replace=False)]))
+    ref, rinfo = ref_moe.moe_forward(x_np, logits_np, w["w13"].numpy(), w["w13_scale"].numpy(),
+                                     w["w2"].numpy(), w["w2_scale"].numpy(), k, True, tokens=tok)
+    pairs = (tok[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    gq, gs = _requant_rows(taps, rows, pairs, T * k)
+    mm = _compare_requant(gq, gs, rinfo["aq"], rinfo["as"])
+    assert mm * gq.size <= 1e-2 * gq.size + 3
+    m = assert_out_close(np_(out.float())[tok], ref, "maximum sizes")
+    note(f"  sampled {tok.size} tokens: max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e}")
