@@ -45,3 +45,34 @@ def test_graph_replay_matches_eager(T, H, I, E, k):
         again = moe.moe_fp8_forward(x, logits, w13, w13s, w2, w2s, k, True, workspace=ws_e)
         torch.cuda.synchronize()
         assert torch.equal(again.view(torch.int16), eager.view(torch.int16)), f"eager after {rep}"
+
+
+def test_graph_replay_batched_experts():
+    """The batched (masked) expert format captured once and replayed with new
+    device-side counts written between replays: each replay equals the eager
+    call on the same counts (graph-capturable decode)."""
+    E, M, H, I = 4, 32, 256, 256
+    note(f"graph capture batched E={E} M={M} H={H} I={I}")
+    w = make_weights(H, I, E, 901, "cuda")
+    g = torch.Generator(device="cpu").manual_seed(902)
+    x = torch.randn((E, M, H), generator=g).to(torch.bfloat16).cuda()
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    n = moe.moe_fp8_batched_workspace_bytes(E, M, H, I)
+    ws_e = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws_g = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out_g = torch.empty_like(x)
+    counts.copy_(torch.tensor([5, 0, 32, 17], dtype=torch.int32))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_fp8_batched_experts(x, counts, *w, out=out_g, workspace=ws_g)
+    torch.cuda.synchronize()
+    for rep, cnt in enumerate([[5, 0, 32, 17], [32, 32, 1, 0], [0, 0, 0, 9], [7, 13, 21, 32]]):
+        counts.copy_(torch.tensor(cnt, dtype=torch.int32))      # eager work between replays
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = moe.moe_fp8_batched_experts(x, counts, *w, workspace=ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), eager.view(torch.int16)), f"replay {rep}, counts {cnt}"
