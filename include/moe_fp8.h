@@ -251,10 +251,12 @@ int moe_fp8_mx_forward(const void* x, const float* router_logits,
 /* Stages of the forward, in launch order (for moe_fp8_forward_traced). */
 enum {
   MOE_STAGE_ROUTER = 0,     /* softmax top-k */
-  MOE_STAGE_ALIGN,          /* sort and pad by expert (three kernels) */
+  MOE_STAGE_ALIGN,          /* sort and pad by expert (one kernel up to 1024 pairs, else three) */
   MOE_STAGE_QUANT,          /* activation quantisation of x */
-  MOE_STAGE_GEMM1,          /* w13 GEMM + SiLU*mul + requantisation */
-  MOE_STAGE_GEMM2,          /* w2 GEMM (per sorted row, before the routing weight) */
+  MOE_STAGE_GEMM1,          /* w13 GEMM + SiLU*mul + requantisation (with K slices: the
+                               partials' kernel and the one that finishes them) */
+  MOE_STAGE_GEMM2,          /* w2 GEMM (per sorted row, or per pair as K-slice partials,
+                               before the routing weight) */
   MOE_STAGE_COMBINE,        /* weighted sum over the top_k slots */
   MOE_STAGE_COUNT
 };
