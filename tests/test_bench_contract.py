@@ -1,0 +1,48 @@
+"""Host-side pieces of bench.py: the algorithmic byte / flop counts the
+roofline uses, the bound selection, and the one-GPU guard."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_algorithmic_counts_by_hand():
+    # 3 tokens, top-2 over 4 experts; experts 0, 2 and 3 are used, 1 is not
+    T, H, I, E, k = 3, 256, 128, 4, 2
+    ids = np.array([[0, 2], [2, 3], [0, 3]])
+    a = bench.algorithmic(ids, T, H, I, E, k)
+    P = T * k
+    w13 = 2 * I * H + 4 * (2 * I // 128) * (H // 128)     # codes + float32 block scales
+    w2 = H * I + 4 * (H // 128) * (I // 128)
+    assert a["active_experts"] == 3
+    assert a["layer_bytes"] == 3 * (w13 + w2) + 2 * T * H + 2 * T * H + 4 * T * E
+    assert a["layer_flops"] == 6 * P * H * I
+    assert a["stage"]["gemm1"][1] == 4 * P * H * I and a["stage"]["gemm2"][1] == 2 * P * H * I
+    # the stages' flops add up to the layer's
+    assert sum(f for _, f in a["stage"].values()) == a["layer_flops"]
+
+
+def test_roofline_bound_selection():
+    # 1 GB and 1 TFLOP in 1 ms: 1 TB/s of 8, 1 PFLOP/s of 5 -> the HBM time
+    # (0.125 ms) is below the MFMA time (0.2 ms), so MFMA-bound
+    r = bench.roofline_of(1e9, 1e12, 1e-3)
+    assert r["bound"] == "mfma" and abs(r["achieved"] - 1000.0) < 1e-9 and abs(r["frac"] - 0.2) < 1e-12
+    r = bench.roofline_of(4e9, 1e9, 1e-3)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and abs(r["frac"] - 0.5) < 1e-12
+    # against the f16 peak the same flops are twice the fraction
+    r = bench.roofline_of(1e9, 1e12, 1e-3, bench.MFMA_F16_PEAK)
+    assert abs(r["frac"] - 0.4) < 1e-12
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
