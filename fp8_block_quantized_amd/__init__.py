@@ -120,6 +120,66 @@ def _dev(t, dtype, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, want, name):
+    """Raise ValueError unless tensor t has exactly the shape want (checked
+    before anything reaches the library, so a mismatched tensor never lets a
+    kernel read or write past an allocation)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} must have shape {tuple(want)}, got {tuple(t.shape)}")
+
+
+def _ndim(t, n, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _same_device(ref, named):
+    for name, t in named.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, x on {ref.device}")
+
+
+def _multiple(v, m, name):
+    if v % m:
+        raise ValueError(f"{name} = {v} must be a multiple of {m}")
+
+
+def _check_moe_tensors(x, router_logits, w13, w13_scale, w2, w2_scale, out, mx=False,
+                       all_experts=True):
+    """Full shape and device checks of a fused-MoE call; returns (T, H, I, E, EL).
+    EL is the expert count of the weights, which must be E when all_experts."""
+    T, H = _ndim(x, 2, "x")
+    T2, E = _ndim(router_logits, 2, "router_logits")
+    if T2 != T:
+        raise ValueError(f"router_logits has {T2} rows, x has {T}")
+    EL, N13, H13 = _ndim(w13, 3, "w13")
+    EL2, H2, I = _ndim(w2, 3, "w2")
+    if EL2 != EL:
+        raise ValueError(f"w2 holds {EL2} experts, w13 {EL}")
+    if all_experts and EL != E:
+        raise ValueError(f"the weights hold {EL} experts, the router logits {E}")
+    _multiple(H, QUANT_GROUP, "hidden size")
+    _multiple(I, QUANT_GROUP, "intermediate size")
+    _shape(w13, (EL, 2 * I, H), "w13")
+    _shape(w2, (EL, H, I), "w2")
+    if mx:
+        _shape(w13_scale, (EL, 2 * I, H // 32), "w13_scale")
+        _shape(w2_scale, (EL, H, I // 32), "w2_scale")
+    else:
+        _shape(w13_scale, (EL, 2 * I // 128, H // 128), "w13_scale")
+        _shape(w2_scale, (EL, H // 128, I // 128), "w2_scale")
+    if out is not None:
+        _shape(out, (T, H), "out")
+    _same_device(x, {"router_logits": router_logits, "w13": w13, "w13_scale": w13_scale,
+                     "w2": w2, "w2_scale": w2_scale, "out": out})
+    return T, H, I, E, EL
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -157,9 +217,7 @@ def moe_fp8_forward(x, router_logits, w13, w13_scale, w2, w2_scale, top_k, renor
     With ``events`` (len(STAGES) + 1 timing-enabled torch.cuda.Event objects
     that have been recorded once), calls moe_fp8_forward_traced, which records
     them around each stage on the launch stream."""
-    T, H = x.shape
-    E = router_logits.shape[1]
-    I = w2.shape[2]
+    T, H, I, E, _ = _check_moe_tensors(x, router_logits, w13, w13_scale, w2, w2_scale, out)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -186,10 +244,11 @@ def moe_fp8_forward_routed(x, router_logits, w13, w13_scale, w2, w2_scale, top_k
                            workspace=None, stream=None):
     """moe_fp8_forward with grouped top-k and/or an expert map (int32 [E] on the
     device, global -> local expert or -1); the weights hold the local experts."""
-    T, H = x.shape
-    E = router_logits.shape[1]
-    I = w2.shape[2]
-    EL = w13.shape[0]
+    T, H, I, E, EL = _check_moe_tensors(x, router_logits, w13, w13_scale, w2, w2_scale, out,
+                                        all_experts=expert_map is None)
+    if expert_map is not None:
+        _shape(expert_map, (E,), "expert_map")
+        _same_device(x, {"expert_map": expert_map})
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -248,7 +307,15 @@ def workspace_taps(workspace, T, H, I, E, top_k, mx=False):
 
 def per_token_group_quant_fp8(x, group_size=128, q=None, scales=None, stream=None):
     """x bf16 [M, K] -> (q uint8 e4m3fn codes [M, K], scales f32 [M, K/group])."""
-    M, K = x.shape
+    M, K = _ndim(x, 2, "x")
+    if group_size != QUANT_GROUP:
+        raise ValueError(f"group_size must be {QUANT_GROUP}")
+    _multiple(K, group_size, "K")
+    if q is not None:
+        _shape(q, (M, K), "q")
+    if scales is not None:
+        _shape(scales, (M, K // group_size), "scales")
+    _same_device(x, {"q": q, "scales": scales})
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if scales is None:
@@ -267,7 +334,17 @@ def per_token_group_quant_fp8_fmt(x, group_size=128, scale_format="float32", q=N
                                   stream=None):
     """x bf16 [M, K] -> (q uint8 e4m3fn codes [M, K], scales [M, K/group]): float32
     scales for "float32" and "float32_ceil_ue8m0", uint8 exponent bytes for "ue8m0"."""
-    M, K = x.shape
+    M, K = _ndim(x, 2, "x")
+    if group_size not in (32, 128):
+        raise ValueError("group_size must be 32 or 128")
+    _multiple(K, group_size, "K")
+    if scale_format not in SCALE_FORMATS:
+        raise ValueError(f"scale_format must be one of {sorted(SCALE_FORMATS)}")
+    if q is not None:
+        _shape(q, (M, K), "q")
+    if scales is not None:
+        _shape(scales, (M, K // group_size), "scales")
+    _same_device(x, {"q": q, "scales": scales})
     fmt = SCALE_FORMATS[scale_format]
     sdt = torch.uint8 if scale_format == "ue8m0" else torch.float32
     if q is None:
@@ -283,7 +360,11 @@ def per_token_group_quant_fp8_fmt(x, group_size=128, scale_format="float32", q=N
 
 def moe_topk_softmax(logits, top_k, renormalize, ids=None, weights=None, stream=None):
     """logits f32 [T, E] -> (ids int32 [T, k], weights f32 [T, k])."""
-    T, E = logits.shape
+    T, E = _ndim(logits, 2, "logits")
+    for name, t in (("ids", ids), ("weights", weights)):
+        if t is not None:
+            _shape(t, (T, top_k), name)
+    _same_device(logits, {"ids": ids, "weights": weights})
     if ids is None:
         ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
     if weights is None:
@@ -298,7 +379,11 @@ def moe_topk_softmax(logits, top_k, renormalize, ids=None, weights=None, stream=
 def moe_topk_softmax_grouped(logits, top_k, num_expert_group, topk_group, renormalize, ids=None,
                              weights=None, stream=None):
     """Grouped top-k: logits f32 [T, E] -> (ids int32 [T, k], weights f32 [T, k])."""
-    T, E = logits.shape
+    T, E = _ndim(logits, 2, "logits")
+    for name, t in (("ids", ids), ("weights", weights)):
+        if t is not None:
+            _shape(t, (T, top_k), name)
+    _same_device(logits, {"ids": ids, "weights": weights})
     if ids is None:
         ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
     if weights is None:
@@ -314,7 +399,7 @@ def moe_topk_softmax_grouped(logits, top_k, num_expert_group, topk_group, renorm
 def moe_align(topk_ids, num_experts, block_m, stream=None):
     """topk_ids int32 [T, k] -> (sorted_ids, expert_ids, num_tokens_post_padded)
     over the full capacity; only the first num_tokens_post_padded rows are defined."""
-    T, k = topk_ids.shape
+    T, k = _ndim(topk_ids, 2, "topk_ids")
     P = T * k
     cap = -(-(P + num_experts * (block_m - 1)) // block_m) * block_m
     dev = topk_ids.device
@@ -339,8 +424,16 @@ def fp8_block_linear_workspace_bytes(M, N, K):
 def fp8_block_linear(x, w, w_scale, out=None, workspace=None, stream=None):
     """Dense block-FP8 linear: x bf16 [M, K], w uint8 e4m3fn [N, K], w_scale f32
     [N/128, K/128] -> out bf16 [M, N] (x quantised per 128-group of each row)."""
-    M, K = x.shape
-    N = w.shape[0]
+    M, K = _ndim(x, 2, "x")
+    N, K2 = _ndim(w, 2, "w")
+    if K2 != K:
+        raise ValueError(f"w has {K2} input features, x has {K}")
+    _multiple(N, 128, "N")
+    _multiple(K, 128, "K")
+    _shape(w_scale, (N // 128, K // 128), "w_scale")
+    if out is not None:
+        _shape(out, (M, N), "out")
+    _same_device(x, {"w": w, "w_scale": w_scale, "out": out})
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -364,8 +457,16 @@ def mxfp8_linear(x, w, w_scale, out=None, workspace=None, stream=None):
     """MXFP8 dense linear: x bf16 [M, K], w uint8 e4m3fn [N, K], w_scale uint8
     UE8M0 exponents [N, K/32] -> out bf16 [M, N] (x quantised per 32-group of
     each row with power-of-two scales)."""
-    M, K = x.shape
-    N = w.shape[0]
+    M, K = _ndim(x, 2, "x")
+    N, K2 = _ndim(w, 2, "w")
+    if K2 != K:
+        raise ValueError(f"w has {K2} input features, x has {K}")
+    _multiple(N, 128, "N")
+    _multiple(K, 128, "K")
+    _shape(w_scale, (N, K // 32), "w_scale")
+    if out is not None:
+        _shape(out, (M, N), "out")
+    _same_device(x, {"w": w, "w_scale": w_scale, "out": out})
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -389,8 +490,20 @@ def moe_fp8_batched_experts(x, expert_num_tokens, w13, w13_scale, w2, w2_scale, 
                             workspace=None, stream=None):
     """Batched (masked) expert format: x bf16 [E, M, H], expert_num_tokens int32
     [E] on the device -> out bf16 [E, M, H] (zero past each count)."""
-    E, M, H = x.shape
+    E, M, H = _ndim(x, 3, "x")
+    _shape(expert_num_tokens, (E,), "expert_num_tokens")
+    _ndim(w2, 3, "w2")
     I = w2.shape[2]
+    _multiple(H, QUANT_GROUP, "hidden size")
+    _multiple(I, QUANT_GROUP, "intermediate size")
+    _shape(w13, (E, 2 * I, H), "w13")
+    _shape(w13_scale, (E, 2 * I // 128, H // 128), "w13_scale")
+    _shape(w2, (E, H, I), "w2")
+    _shape(w2_scale, (E, H // 128, I // 128), "w2_scale")
+    if out is not None:
+        _shape(out, (E, M, H), "out")
+    _same_device(x, {"expert_num_tokens": expert_num_tokens, "w13": w13, "w13_scale": w13_scale,
+                     "w2": w2, "w2_scale": w2_scale, "out": out})
     if out is None:
         out = torch.empty((E, M, H), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
@@ -416,9 +529,8 @@ def moe_fp8_mx_forward(x, router_logits, w13, w13_scale, w2, w2_scale, top_k, re
                        out=None, workspace=None, stream=None):
     """MXFP8 MoE forward: w13 uint8 [E, 2I, H] with UE8M0 bytes [E, 2I, H/32],
     w2 uint8 [E, H, I] with UE8M0 bytes [E, H, I/32]."""
-    T, H = x.shape
-    E = router_logits.shape[1]
-    I = w2.shape[2]
+    T, H, I, E, _ = _check_moe_tensors(x, router_logits, w13, w13_scale, w2, w2_scale, out,
+                                       mx=True)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if workspace is None:

@@ -167,7 +167,8 @@ def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         moe.per_token_group_quant_fp8(torch.zeros((2, 128), dtype=torch.bfloat16),
-                                      q=torch.zeros(1), scales=torch.zeros(1))
+                                      q=torch.zeros((2, 128), dtype=torch.uint8),
+                                      scales=torch.zeros((2, 1)))
 
 
 def test_linear_workspace_and_argument_checks():
