@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_fp8.so")
 
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
-          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIAS"}
+          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_ALIAS", -7: "MOE_ERR_SCRATCH"}
 TAPS = ["topk_ids", "topk_weights", "sorted_ids", "expert_ids", "ntpp", "pair_pos", "xq", "xs",
         "aq", "as", "y", "align_scratch", "y_slices", "h_slices"]
 MAX_EXPERTS = 512
@@ -31,7 +31,8 @@ EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layo
            "per_token_group_quant_fp8_fmt", "moe_topk_softmax", "moe_topk_softmax_grouped",
            "moe_fp8_forward_routed", "moe_fp8_batched_workspace_bytes", "moe_fp8_batched_experts",
            "moe_fp8_mx_workspace_bytes", "moe_fp8_mx_workspace_layout", "moe_fp8_mx_forward",
-           "moe_align_scratch_bytes", "moe_align", "moe_status_string",
+           "moe_align_scratch_bytes", "moe_align", "moe_align_noalloc",
+           "moe_align_noalloc_max_scratch_bytes", "moe_status_string",
            "fp8_block_linear_workspace_bytes", "fp8_block_linear",
            "mxfp8_linear_workspace_bytes", "mxfp8_linear", "moe_mfma_rate_probe"]
 
@@ -89,6 +90,10 @@ def load_library(path=LIB_PATH):
     lib.moe_align_scratch_bytes.restype = c_size
     lib.moe_align.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp, c_size, vp]
     lib.moe_align.restype = c_int
+    lib.moe_align_noalloc.argtypes = [vp, c_int, c_int, c_int, c_int, vp, vp, vp, vp]
+    lib.moe_align_noalloc.restype = c_int
+    lib.moe_align_noalloc_max_scratch_bytes.argtypes = []
+    lib.moe_align_noalloc_max_scratch_bytes.restype = c_size
     lib.fp8_block_linear_workspace_bytes.argtypes = [c_int] * 3
     lib.fp8_block_linear_workspace_bytes.restype = c_size
     lib.fp8_block_linear.argtypes = [vp, vp, vp, c_int, c_int, c_int, vp, vp, c_size, vp]
@@ -417,6 +422,34 @@ def moe_align(topk_ids, num_experts, block_m, stream=None):
     return sorted_ids, expert_ids, ntpp
 
 
+def moe_align_noalloc(topk_ids, num_experts, block_m, sorted_ids=None, expert_ids=None,
+                      ntpp=None, stream=None):
+    """moe_align with the library's fixed per-GPU scratch instead of a scratch
+    tensor: the call itself allocates no device memory.  Output tensors
+    (sorted_ids int32 [cap], expert_ids int32 [cap / block_m], ntpp int32 [1])
+    may be passed in to keep the call allocation-free on the Python side too."""
+    T, k = _ndim(topk_ids, 2, "topk_ids")
+    P = T * k
+    cap = -(-(P + num_experts * (block_m - 1)) // block_m) * block_m
+    dev = topk_ids.device
+    if sorted_ids is None:
+        sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    if expert_ids is None:
+        expert_ids = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
+    if ntpp is None:
+        ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+    _shape(sorted_ids, (cap,), "sorted_ids")
+    _shape(expert_ids, (cap // block_m,), "expert_ids")
+    _shape(ntpp, (1,), "ntpp")
+    _same_device(topk_ids, {"sorted_ids": sorted_ids, "expert_ids": expert_ids, "ntpp": ntpp})
+    st = load_library().moe_align_noalloc(
+        _dev(topk_ids, torch.int32, "topk_ids"), T, k, num_experts, block_m,
+        _dev(sorted_ids, torch.int32, "sorted_ids"), _dev(expert_ids, torch.int32, "expert_ids"),
+        _dev(ntpp, torch.int32, "ntpp"), _stream(stream))
+    _check("moe_align_noalloc", st)
+    return sorted_ids, expert_ids, ntpp
+
+
 def fp8_block_linear_workspace_bytes(M, N, K):
     return load_library().fp8_block_linear_workspace_bytes(M, N, K)
 
@@ -563,3 +596,4 @@ def moe_mfma_rate_probe(kind, iters, nblocks, sink, stream=None):
                                             _dev(sink, torch.float32, "sink"), _stream(stream))
     _check("moe_mfma_rate_probe", st)
     return nblocks * 4 * iters * 8 * MFMA_PROBE_FLOPS[kind]
+

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 
 namespace {
@@ -185,6 +187,41 @@ void make_linear_layout(int M, int N, int K, LinearLayout& L) {
 
 }  // namespace
 
+// Scratch of the scratch-free sort-and-pad (moe_align_noalloc): a file-scope
+// device array sized for the largest call the ABI accepts (MOE_MAX_TOKENS *
+// MOE_MAX_TOP_K pairs in 1024-pair chunks, MOE_MAX_EXPERTS experts: per-chunk
+// counts and bases, then the expert block offsets).  Every GPU the library
+// runs on holds its own copy, created with the code object and kept until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): it asks the runtime for the
+// current device's address of it once per device and uses that.
+namespace moe_noalloc {
+constexpr size_t kChunkPairs = 1024;
+constexpr size_t kScratchInts =
+    2 * ((size_t)MOE_MAX_TOKENS * MOE_MAX_TOP_K / kChunkPairs) * MOE_MAX_EXPERTS + MOE_MAX_EXPERTS + 1;
+__device__ __attribute__((aligned(256))) int32_t scratch[kScratchInts];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+void* g_ptr[kMaxDevices];   // device address of scratch on each device, once looked up
+
+// Address of `scratch` on the current device: looked up on the first call
+// on that device (with that device current), then reused.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_ptr[dev] = p;
+  }
+  *out = g_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace moe_noalloc
+
 extern "C" {
 
 const char* moe_status_string(int status) {
@@ -196,6 +233,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_HIP: return "HIP runtime error at launch";
     case MOE_ERR_ALIAS: return "an output overlaps an input or the workspace";
+    case MOE_ERR_SCRATCH: return "request exceeds the fixed scratch of a scratch-free entry point";
     default: return "unknown status";
   }
 }
@@ -588,6 +626,37 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m, int
   const int P = T * top_k;
   if (scratch_bytes < moe::align_scratch_bytes(P, E) || ((uintptr_t)scratch % 4))
     return MOE_ERR_WORKSPACE;
+  return moe::launch_align(topk_ids, nullptr, 0, P, E, block_m, sorted_ids, expert_ids,
+                           num_tokens_post_padded, nullptr, scratch, stream)
+             ? MOE_ERR_HIP
+             : MOE_OK;
+}
+
+size_t moe_align_noalloc_max_scratch_bytes(void) {
+  return sizeof(moe_noalloc::scratch);
+}
+
+int moe_align_noalloc(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+                      int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                      hipStream_t stream) {
+  if (T < 0 || top_k < 1 || E < 1 || E > MOE_MAX_EXPERTS || top_k > E) return MOE_ERR_SHAPE;
+  if ((long long)T * top_k > (long long)MOE_MAX_TOKENS * MOE_MAX_TOP_K) return MOE_ERR_SHAPE;
+  if (block_m < 16 || block_m > 256 || (block_m & (block_m - 1))) return MOE_ERR_SHAPE;
+  if (!sorted_ids || !expert_ids || !num_tokens_post_padded) return MOE_ERR_NULL;
+  if (T > 0 && !topk_ids) return MOE_ERR_NULL;
+  const int P = T * top_k;
+  if (moe::align_scratch_bytes(P, E) > sizeof(moe_noalloc::scratch)) return MOE_ERR_SCRATCH;
+  if (stream) {            // the scratch looked up must be the stream's device's copy
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (cur != sdev) return MOE_ERR_UNSUPPORTED;
+  }
+  void* scratch = nullptr;
+  const int st = moe_noalloc::scratch_on_current_device(&scratch);
+  if (st != MOE_OK) return st;
+  // the kernels write every scratch word they read (counts, then bases and
+  // offsets), so nothing is cleared between calls
   return moe::launch_align(topk_ids, nullptr, 0, P, E, block_m, sorted_ids, expert_ids,
                            num_tokens_post_padded, nullptr, scratch, stream)
              ? MOE_ERR_HIP

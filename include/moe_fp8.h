@@ -26,8 +26,10 @@
  *   - Scales are float32 dequant multipliers: value = dec(code) * scale.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without synchronising.  The library allocates no device memory
- *     and keeps no mutable global state; calls on different streams with
- *     disjoint outputs and workspaces may run concurrently.
+ *     and keeps no mutable global state (the one exception is the fixed
+ *     per-GPU scratch of moe_align_noalloc, described there); calls on
+ *     different streams with disjoint outputs and workspaces may run
+ *     concurrently.
  *   - Arguments are validated on the host before anything is launched; a
  *     negative moe_status is returned on error and nothing is enqueued.  A
  *     launch failure reported by the HIP runtime returns MOE_ERR_HIP.  On any
@@ -53,7 +55,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = -3, /* a valid request this library does not serve */
   MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_fp8_workspace_bytes() */
   MOE_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
-  MOE_ERR_ALIAS = -6        /* an output overlaps an input or the workspace */
+  MOE_ERR_ALIAS = -6,       /* an output overlaps an input or the workspace */
+  MOE_ERR_SCRATCH = -7      /* the request exceeds the fixed scratch of a scratch-free entry point */
 } moe_status;
 
 /* Limits.  H and I must be multiples of 128 (the weight block and activation
@@ -361,6 +364,27 @@ int moe_align(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
               int32_t* sorted_ids, int32_t* expert_ids,
               int32_t* num_tokens_post_padded,
               void* scratch, size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * moe_align without a scratch argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and outputs as
+ * moe_align; the scratch is a fixed device array inside the library (one per
+ * GPU, created with the library's code object and held until the process
+ * ends) of moe_align_noalloc_max_scratch_bytes() bytes, about 2.1 MB: enough
+ * for every shape moe_align accepts (T*top_k <= MOE_MAX_TOKENS*MOE_MAX_TOP_K,
+ * E <= MOE_MAX_EXPERTS).  A request that would need more returns
+ * MOE_ERR_SCRATCH.  The call allocates nothing and enqueues no memset; the
+ * first call on a device looks up that device's copy of the array (the device
+ * must be current, and a non-NULL stream must belong to it, else
+ * MOE_ERR_UNSUPPORTED).  All calls on one GPU share its one array: calls that
+ * may overlap on a GPU (on different streams, or concurrently from several
+ * host threads) race on it and must be serialised by the caller.
+ */
+size_t moe_align_noalloc_max_scratch_bytes(void);
+int moe_align_noalloc(const int32_t* topk_ids, int T, int top_k, int E, int block_m,
+                      int32_t* sorted_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_padded, hipStream_t stream);
 
 /*
  * Dense block-FP8 linear layer (overview page, "W8A8BlockFp8LinearOp - Block

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = moe.load_library()
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert lib.moe_status_string(code)
     assert lib.moe_status_string(7) == b"unknown status"
 
@@ -305,3 +305,21 @@ def test_mfma_probe_argument_checks():
     assert f(0, 10, 4, None, None) == -1          # no sink
     assert f(1, 10, 4, vp(0x7000000002), None) == -3   # misaligned sink
     assert moe.MFMA_PROBE_FLOPS == {"f16": 16 * 16 * 32 * 2, "fp8": 16 * 16 * 128 * 2}
+
+
+def test_noalloc_align_scratch_limit_and_argument_checks():
+    """The scratch-free sort-and-pad: its fixed scratch covers the largest
+    request moe_align accepts, and its arguments are checked on the host
+    before the device scratch is looked up (no HIP call here)."""
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    assert lib.moe_align_noalloc_max_scratch_bytes() == lib.moe_align_scratch_bytes(
+        moe.MAX_TOKENS, moe.MAX_TOP_K, moe.MAX_EXPERTS)
+    ok = (vp(16), 64, 8, 256, 16, vp(64), vp(128), vp(256), None)
+    assert lib.moe_align_noalloc(*ok[:4], 24, *ok[5:]) == -2           # block_m not a power of 2
+    assert lib.moe_align_noalloc(ok[0], 64, 8, 513, 16, *ok[5:]) == -2  # too many experts
+    assert lib.moe_align_noalloc(ok[0], moe.MAX_TOKENS + 1, moe.MAX_TOP_K, 512, 16, *ok[5:]) == -2
+    assert lib.moe_align_noalloc(None, *ok[1:]) == -1
+    assert lib.moe_align_noalloc(*ok[:5], None, *ok[6:]) == -1
+    assert lib.moe_status_string(-7) != b"unknown status"
+
