@@ -157,6 +157,7 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
         flat = expert_map[flat]                  # local expert, -1 where absent
         E = w13.shape[0]
     y = np.zeros((P, H), dtype=np.float64)
+    h = np.zeros((P, 2 * I), dtype=np.float64)
     a = np.zeros((P, I), dtype=np.float32)
     aq = np.zeros((P, I), dtype=np.uint8)
     as_ = (np.zeros((P, I // 32), dtype=np.uint8) if mx
@@ -167,6 +168,7 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
             continue
         r = ffn(x[pairs // top_k], w13[e], w13_scale[e], w2[e], w2_scale[e])
         y[pairs] = r["y"]
+        h[pairs] = r["h"]
         a[pairs] = r["a"]
         aq[pairs] = r["aq"]
         as_[pairs] = r["as"]
@@ -175,9 +177,42 @@ def moe_forward(x, logits, w13, w13_scale, w2, w2_scale, top_k: int,
     for j in range(top_k):
         acc += w[:, j:j + 1].astype(np.float64) * y[j::top_k]
     out = bf16_round(acc)
-    info = {"ids": ids, "w": w, "xq": xq, "xs": xs, "a": a, "aq": aq,
+    info = {"ids": ids, "w": w, "xq": xq, "xs": xs, "h": h, "a": a, "aq": aq,
             "as": as_, "y": y}
     return out, info
+
+
+def finish_from_requant(aq, as_, ids, w, w2, w2_scale, top_k: int, expert_map=None):
+    """Steps 7 and 8 of the definition applied to given requantised
+    activations: the second GEMM and the weighted combine, in float64.
+
+    aq uint8 [P, I] and as_ float32 [P, I/128] are the requantised activation
+    of every pair p = t * top_k + j (pair order), ids / w the routing [T, k].
+    With the oracle's own (aq, as) this is the tail of moe_forward, value for
+    value.  It exists because the requantisation of step 6 is a step function
+    of a: where a / s lies on a rounding midpoint to within the first GEMM's
+    accumulation error, either neighbouring code is a correct result of the
+    method (its sums are defined up to rounding order), and the layer's output
+    is then this function of the codes actually chosen.
+
+    Returns out float32 [T, H] holding bf16 values."""
+    ids = np.asarray(ids)
+    T = ids.shape[0]
+    H = w2.shape[1]
+    flat = ids.reshape(-1)
+    if expert_map is not None:
+        flat = np.asarray(expert_map, dtype=np.int64)[flat]
+    y = np.zeros((T * top_k, H), dtype=np.float64)
+    for e in range(w2.shape[0]):
+        pairs = np.nonzero(flat == e)[0]
+        if pairs.size == 0:
+            continue
+        Af = quant.dequant(aq[pairs], as_[pairs])
+        y[pairs] = Af @ quant.block_dequant(w2[e], w2_scale[e]).T
+    acc = np.zeros((T, H), dtype=np.float64)
+    for j in range(top_k):
+        acc += np.asarray(w)[:, j:j + 1].astype(np.float64) * y[j::top_k]
+    return bf16_round(acc)
 
 
 def batched_experts(x, counts, w13, w13_scale, w2, w2_scale):

@@ -18,7 +18,7 @@ import torch
 from scipy.special import softmax
 
 from oracle import moe, quant, router
-from synth import make_activations, make_weights
+from synth import make_activations, make_weights, moe_workload
 from tests import _brute
 
 DEC = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -339,3 +339,22 @@ def test_mx_layer_loosely_matches_the_unquantised_mlp():
             ref[t] += float(info["w"][t, j]) * (wf2[e].double().numpy() @ a)
     rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
     assert rel < 0.1, rel
+
+
+def test_finish_from_requant_is_the_forward_tail():
+    """Steps 7-8 from given requantised codes: fed the forward's own codes it
+    reproduces the forward's output bit for bit; fed the codes of a different
+    pair for one pair, that pair's token changes and no other token does."""
+    w = moe_workload("tiny", 16)
+    x, lg = w["x"].float().numpy(), w["logits"].numpy()
+    args = (w["w13"].numpy(), w["w13_scale"].numpy(), w["w2"].numpy(), w["w2_scale"].numpy())
+    k = w["top_k"]
+    out, info = moe.moe_forward(x, lg, *args, k, True)
+    again = moe.finish_from_requant(info["aq"], info["as"], info["ids"], info["w"], args[2],
+                                        args[3], k)
+    assert np.array_equal(again.view(np.uint32), out.view(np.uint32))
+    aq = info["aq"].copy()
+    aq[5] = info["aq"][9]                          # pair 5 (token 2) takes pair 9's codes
+    other = moe.finish_from_requant(aq, info["as"], info["ids"], info["w"], args[2], args[3], k)
+    changed = np.nonzero(np.any(other != out, axis=1))[0]
+    assert changed.tolist() == [5 // k]
