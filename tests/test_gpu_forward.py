@@ -4,23 +4,40 @@ against the oracle.
 Exact targets, read from the documented workspace taps: routing ids, the
 sort-and-pad layout and the activation codes and scales.  The routing
 weights match within 1e-5 relative.  The requantised activation is not an
-exact target: its codes depend on how the first GEMM accumulates.  GEMM1's
-block partials are exact (f16 MFMAs of exactly converted e4m3 operands); the
-decode kernels fold them in float64, the 128-row prefill kernel in float32,
-whose rounding (a few 1e-7 of h) moves a code next to a rounding midpoint
-now and then.  The test requires fewer than 1% (+3) differing codes, each
-within one grid step of the oracle's plus 1/8 in units of the group scale,
-and requant scales within 1e-3 relative.  The bf16 output must satisfy
-|gpu - ref| <= 1e-2 + 2e-2 |ref| everywhere and a relative norm error below
-1e-2: the expected difference is a few 1e-3, from the bf16 rounding of the
-per-pair outputs before the combine, GEMM2's FP8 accumulation and the rare
-requant code flips.
+exact target.  It is a step function of a, and a's sums are defined only up
+to rounding order: GEMM1's block partials are exact products summed by f16
+MFMAs in float32, folded in float64 (decode kernels, block_m <= 64) or float32
+(the 128-row prefill kernel), so h carries a relative error of ~1e-7 of the
+row's largest values.  Where the oracle's a / s lies on a rounding midpoint
+to within that error, both neighbouring codes are correct results of the
+method.  The test therefore compares what is unique and checks that the rest
+is valid:
+  * requant scales agree to 1e-5 relative;
+  * a code that differs from the oracle's is one e4m3 grid step away, and the
+    oracle's quotient a / s lies within the tie window of the midpoint
+    between the two codes (the window bounds the kernels' error of h by 2^-18
+    of the largest |h| of the row's 128-feature group, propagated through
+    SiLU*mul and the scale); at most 1e-4 of the codes (+8) differ;
+  * the output equals, within the bar, the oracle's second GEMM and combine
+    applied to the GPU's own requantised codes (oracle.moe.finish_from_requant),
+    on every compared token;
+  * on every token none of whose pairs took a tie the other way, the output
+    also meets the bar against the oracle's own output, and the relative norm
+    error over all compared tokens is below 1e-2.
+The bar is |gpu - ref| <= 1e-2 + 2e-2 |ref| everywhere plus a relative norm
+error below 1e-2: the expected difference is a few 1e-3, from the bf16
+rounding of the per-pair outputs before the combine and GEMM2's FP8
+accumulation.
 
-Small layers are compared on every output; the full-size workloads, run
-exactly as the benchmark runs them, are compared on sampled tokens (each
-token's output depends only on its own row, and the requantised rows of the
-sampled tokens' pairs are compared too), with the routing, layout and
-activation codes still checked on every token."""
+Every output and every requantised row is compared, at every size the oracle
+finishes in seconds: the small layers, a layer whose persistent second GEMM
+runs several tiles per workgroup, and the full-size workloads exactly as the
+benchmark runs them (Mixtral- and Qwen3-shaped at every batch size, the
+DeepSeek-V3-shaped decode batch).  Only the DeepSeek-V3-shaped prefill batch
+(5.8 TFLOP in the oracle) is compared on sampled tokens (each token's output
+depends only on its own row, and the requantised rows of the sampled tokens'
+pairs are compared too), with the routing, layout and activation codes still
+checked on every token."""
 
 import numpy as np
 import pytest
@@ -54,16 +71,68 @@ def _check_taps(taps, info, ids_np, E, what):
     return gs
 
 
-def _compare_requant(g, gs, r, rs):
-    """fraction of requantised codes g (e4m3 codes, [n, I]) that differ from
-    the oracle's r; asserts every difference is within one grid step + 1/8
-    and the scales gs agree with rs to 1e-3"""
-    np.testing.assert_allclose(gs, rs, rtol=1e-3, atol=0)
+# at most this fraction (+ count) of the requantised codes may take a tie the other way
+REQUANT_TIES = (1e-4, 8)
+H_ERR = 2.0 ** -18          # bound on the kernels' error of h, relative to the group's largest |h|
+
+
+def _tie_window(h, a, s, I):
+    """Per element of the requantised activation, the half-width (in units of
+    the group scale s) within which a / s may sit from a rounding midpoint and
+    still round either way under the kernels' accumulation error.
+    h float64 [n, 2I] (gate, up), a float32 [n, I], s float32 [n, I/128]."""
+    n = a.shape[0]
+    gt, up = h[:, :I], h[:, I:]
+    hmax = np.maximum(np.abs(gt), np.abs(up)).reshape(n, I // 128, 128).max(axis=2)
+    err_h = H_ERR * np.repeat(hmax, 128, axis=1)
+    silu_g = ref_moe.silu(gt)
+    err_a = (1.1 * np.abs(up) + np.abs(silu_g)) * err_h + 2.0 ** -21 * np.abs(a)
+    a_abs = np.abs(a.astype(np.float64)).reshape(n, I // 128, 128)
+    arg = a_abs.argmax(axis=2)
+    amax = np.take_along_axis(a_abs, arg[..., None], axis=2)[..., 0]
+    err_amax = np.take_along_axis(err_a.reshape(n, I // 128, 128), arg[..., None], axis=2)[..., 0]
+    err_s_rel = err_amax / np.maximum(amax, 1e-30) + 2.0 ** -23
+    s_full = np.repeat(s.astype(np.float64), 128, axis=1)
+    q = a / s_full
+    return err_a / s_full + np.abs(q) * np.repeat(err_s_rel, 128, axis=1), q
+
+
+def _check_requant(g, gs, rinfo, pairs_ref, I, what=""):
+    """GPU requantised codes g [n, I] and scales gs of the oracle's pairs
+    pairs_ref against the oracle (rinfo: moe_forward's info over the same
+    tokens).  Returns a boolean [n] marking pairs with a code that took a tie
+    the other way."""
+    r, rs = rinfo["aq"][pairs_ref], rinfo["as"][pairs_ref]
+    np.testing.assert_allclose(gs, rs, rtol=1e-5, atol=0)
     dg, dr = e4m3.decode(g), e4m3.decode(r)
-    allowed = 2 * e4m3.half_ulp(np.maximum(np.abs(dg), np.abs(dr))) + 0.125
+    allowed = 2 * e4m3.half_ulp(np.maximum(np.abs(dg), np.abs(dr)))
     worst = np.max(np.abs(dg - dr) - allowed)
-    assert worst <= 0, f"a requantised code is {worst} beyond one grid step + 1/8"
-    return float(np.mean(g != r))
+    assert worst <= 0, f"{what}: a requantised code is {worst} beyond one grid step"
+    diff = g != r
+    n_diff = int(diff.sum())
+    if n_diff:
+        win, q = _tie_window(rinfo["h"][pairs_ref], rinfo["a"][pairs_ref], rs, I)
+        mid = 0.5 * (dg + dr)
+        off = np.abs(q - mid)[diff] - win[diff]
+        assert np.max(off) <= 0, (
+            f"{what}: a requantised code differs away from a rounding tie "
+            f"(|a/s - midpoint| exceeds the window by {np.max(off)})")
+    frac, cnt = REQUANT_TIES
+    assert n_diff <= frac * g.size + cnt, f"{what}: {n_diff} of {g.size} requantised codes differ"
+    return diff.any(axis=1)
+
+
+def _check_output(out_gpu, ref, tie_pairs, g_codes, g_scales, rinfo, w2, w2s, k, what=""):
+    """out_gpu [n_tok, H] of the compared tokens; ref the oracle's output for
+    them; tie_pairs [n_tok * k] from _check_requant; g_codes / g_scales the
+    GPU's requantised rows of those pairs in pair order."""
+    cont = ref_moe.finish_from_requant(g_codes, g_scales, rinfo["ids"], rinfo["w"], w2, w2s, k)
+    m = assert_out_close(out_gpu, cont, f"{what} (second GEMM and combine from the GPU's codes)")
+    clean = ~tie_pairs.reshape(-1, k).any(axis=1)
+    assert_out_close(out_gpu[clean], ref[clean], f"{what} (tokens with no tie taken the other way)")
+    rel = float(np.linalg.norm(out_gpu - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert rel < 1e-2, f"{what}: relative norm error {rel}"
+    return m, int((~clean).sum())
 
 
 def _requant_rows(taps, sorted_rows, pairs, P):
@@ -78,27 +147,23 @@ def _requant_rows(taps, sorted_rows, pairs, P):
     return np_(taps["aq"][idx]), np_(taps["as"][idx])
 
 
-def _requant_mismatch(taps, info, sorted_rows, P, I):
-    """fraction of differing requantised codes over all pairs"""
-    g, gs = _requant_rows(taps, sorted_rows, np.arange(P), P)
-    return _compare_requant(g, gs, info["aq"], info["as"])
-
-
 def _full_case(w, renorm=True, what=""):
     T, H, I, E, k = w["T"], w["H"], w["I"], w["E"], w["top_k"]
     g = to_dev(w)
     note(f"forward {what} T={T} H={H} I={I} E={E} k={k} renorm={renorm}")
     out, taps, _ = _run(g, T, H, I, E, k, renorm)
+    w2, w2s = w["w2"].numpy(), w["w2_scale"].numpy()
     ref, info = ref_moe.moe_forward(w["x"].float().numpy(), w["logits"].numpy(), w["w13"].numpy(),
-                                    w["w13_scale"].numpy(), w["w2"].numpy(), w["w2_scale"].numpy(),
-                                    k, renorm)
+                                    w["w13_scale"].numpy(), w2, w2s, k, renorm)
     rows = _check_taps(taps, info, info["ids"], E, what)
     assert np.array_equal(np_(taps["xq"]), info["xq"]), f"{what}: xq"
     assert np.array_equal(np_(taps["xs"]).view(np.uint32), info["xs"].view(np.uint32)), f"{what}: xs"
-    mm = _requant_mismatch(taps, info, rows, T * k, I)
-    assert mm * T * k * I <= 1e-2 * T * k * I + 3, f"{what}: requant code mismatch fraction {mm}"
-    m = assert_out_close(np_(out.float()), ref, what)
-    note(f"  max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e} requant_mismatch={mm:.2e}")
+    P = T * k
+    gq, gs = _requant_rows(taps, rows, np.arange(P), P)
+    ties = _check_requant(gq, gs, info, np.arange(P), I, what)
+    m, n_tie = _check_output(np_(out.float()), ref, ties, gq, gs, info, w2, w2s, k, what)
+    note(f"  max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e} "
+         f"ties_other_way={int(ties.sum())} pairs, {n_tie} tokens")
     return out
 
 
@@ -125,11 +190,33 @@ def test_small_layers(T, H, I, E, k, renorm):
     _full_case(_layer(T, H, I, E, k, seed=T + H + I + E + k), renorm, what="small")
 
 
-def test_deterministic():
-    w = to_dev(_layer(64, 512, 256, 8, 2, seed=11))
-    a, _, _ = _run(w, 64, 512, 256, 8, 2, True)
-    b, _, _ = _run(w, 64, 512, 256, 8, 2, True)
+def test_persistent_multi_tile():
+    """128-row blocks with small H and I: the persistent second GEMM (one
+    workgroup per CU) has 8 * 68 = 544 tiles in use, so every workgroup runs
+    two or three tiles back to back and the hand-counted waits between one
+    tile's stores and the next tile's loads are exercised; every output and
+    every requantised row is compared."""
+    T, H, I, E, k = 4096, 2048, 256, 4, 2
+    assert moe.moe_fp8_block_m(T, H, I, E, k) == 128
+    _full_case(_layer(T, H, I, E, k, seed=4242), what="persistent multi-tile")
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (64, 512, 256, 8, 2),        # decode kernels, one workgroup per tile
+    (4096, 2048, 256, 4, 2),     # 128-row prefill kernels, persistent GEMM2 with several tiles each
+    (3, 512, 512, 64, 8),        # K slices of both GEMMs and the combine over them
+])
+def test_deterministic(T, H, I, E, k):
+    w = to_dev(_layer(T, H, I, E, k, seed=11 + T))
+    note(f"determinism T={T} H={H} I={I} E={E} k={k}")
+    a, ta, _ = _run(w, T, H, I, E, k, True)
+    a = a.clone()
+    aq = ta["aq"].clone()
+    b, tb, _ = _run(w, T, H, I, E, k, True)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    rows, _, _ = align_prefix(ta["sorted_ids"], ta["expert_ids"], ta["ntpp"], ta["block_m"])
+    real = torch.from_numpy(np.nonzero(rows < T * k)[0]).cuda()
+    assert torch.equal(aq[real], tb["aq"][real])
 
 
 _FULL = [("mixtral", 64), ("mixtral", 512), ("dsv3", 64), ("dsv3", 8192),
@@ -166,8 +253,11 @@ def test_full_size_workloads(name, T):
     x_np = np_(x.float())
     xq, xs = ref_quant.per_token_group_quant(x_np)
     assert np.array_equal(np_(taps["xq"]), xq) and np.array_equal(np_(taps["xs"]), xs)
-    ns = min(T, 4 if name == "dsv3" else 8)
-    tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(T).choice(T, ns, replace=False)]))
+    sampled = name == "dsv3" and T > 64
+    if sampled:
+        tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(T).choice(T, 14, replace=False)]))
+    else:
+        tok = np.arange(T)
     experts = np.unique(rids[tok])
     sel = torch.from_numpy(experts).cuda()
     w13_np = np.zeros((E,) + tuple(w13.shape[1:]), np.uint8)
@@ -175,14 +265,15 @@ def test_full_size_workloads(name, T):
     w13_np[experts] = np_(w13[sel])
     w2_np[experts] = np_(w2[sel])
     ref, rinfo = ref_moe.moe_forward(x_np, logits_np, w13_np, np_(w13s), w2_np, np_(w2s), k, True,
-                                     tokens=tok)
+                                     tokens=tok if sampled else None)
     pairs = (tok[:, None] * k + np.arange(k)[None, :]).reshape(-1)
-    g, gs = _requant_rows(taps, rows, pairs, T * k)
-    mm = _compare_requant(g, gs, rinfo["aq"], rinfo["as"])
-    assert mm * g.size <= 1e-2 * g.size + 3, f"{name} T={T}: requant code mismatch fraction {mm}"
-    m = assert_out_close(np_(out.float())[tok], ref, f"{name} T={T}")
-    note(f"  sampled {tok.size} tokens: max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e} "
-         f"requant_mismatch={mm:.2e} ({int(round(mm * g.size))} of {g.size} codes)")
+    gq, gs = _requant_rows(taps, rows, pairs, T * k)
+    what = f"{name} T={T}"
+    ties = _check_requant(gq, gs, rinfo, np.arange(pairs.size), I, what)
+    m, n_tie = _check_output(np_(out.float())[tok], ref, ties, gq, gs, rinfo, w2_np, np_(w2s), k, what)
+    note(f"  {'sampled ' if sampled else 'all '}{tok.size} tokens: max|d|={m['max_abs']:.3e} "
+         f"rel_norm={m['rel_norm']:.3e} ties_other_way={int(ties.sum())} pairs, {n_tie} tokens "
+         f"(of {gq.size} codes)")
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [
@@ -234,7 +325,7 @@ def test_maximum_sizes():
                                      w["w2"].numpy(), w["w2_scale"].numpy(), k, True, tokens=tok)
     pairs = (tok[:, None] * k + np.arange(k)[None, :]).reshape(-1)
     gq, gs = _requant_rows(taps, rows, pairs, T * k)
-    mm = _compare_requant(gq, gs, rinfo["aq"], rinfo["as"])
-    assert mm * gq.size <= 1e-2 * gq.size + 3
-    m = assert_out_close(np_(out.float())[tok], ref, "maximum sizes")
+    ties = _check_requant(gq, gs, rinfo, np.arange(pairs.size), I, "maximum sizes")
+    m, _ = _check_output(np_(out.float())[tok], ref, ties, gq, gs, rinfo, w["w2"].numpy(),
+                         w["w2_scale"].numpy(), k, "maximum sizes")
     note(f"  sampled {tok.size} tokens: max|d|={m['max_abs']:.3e} rel_norm={m['rel_norm']:.3e}")

@@ -91,6 +91,7 @@ def _requant_of_pairs(taps, rows, pairs, P):
     (64, 512, 1024, 4, 2),     # 64-row blocks on the 16-byte exponent groups, 8 K blocks in GEMM2
     (40, 1024, 640, 8, 2),     # grouped exponents in GEMM1, per-block bytes in GEMM2 (5 K blocks)
     (20, 256, 256, 64, 6),     # many small experts, heavy padding
+    (4096, 2048, 256, 4, 2),   # 128-row blocks, 544 GEMM2 tiles: several per persistent workgroup
 ])
 @pytest.mark.parametrize("spread", [False, True])
 def test_mx_small_layers(T, H, I, E, k, spread):
