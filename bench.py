@@ -1,19 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of the fused FP8 block-quantized MoE forward on one MI355X.
 
-Workload (default "dsv3"): a DeepSeek-V3-shaped routed-expert layer, H=7168,
-I=2048, E=256, top_k=8 softmax routing with renormalisation and a seeded
-+-0.5 per-expert logit bias (load skew), FP8 e4m3fn weights with 128x128
-block scales (~11.3 GB, drawn N(0, 0.02)), bf16 activations N(0, 1) with
-dynamic per-token 128-group quantisation.  One step = one decode batch of
-T=64 tokens plus one prefill batch of T=8192 tokens through the whole path
-(router, sort-and-pad, activation quant, GEMM1 + SiLU*mul + requant, GEMM2 +
-routing weight, combine).  Inputs are resident in HBM before timing starts.
-The standalone activation quantiser is also timed on its own workload, bf16
-[16384, 7168] with 1% x100 outliers, and the dense block-FP8 linear on a
-DeepSeek-V3-shaped down projection (7168 x 18432) at M = 64 and 8192.
+Headline workload (one "step"): a DeepSeek-V3-shaped routed-expert layer,
+H=7168, I=2048, E=256, top_k=8 softmax routing with renormalisation and a
+seeded +-0.5 per-expert logit bias (load skew), FP8 e4m3fn weights with
+128x128 block scales (~11.3 GB, drawn N(0, 0.02)), bf16 activations N(0, 1)
+with dynamic per-token 128-group quantisation; one decode batch of T=64
+tokens plus one prefill batch of T=8192 tokens through the whole path
+(router, sort-and-pad, activation quant, GEMM1 + SiLU*mul + requant, GEMM2,
+routing-weighted combine).  Inputs are resident in HBM before timing starts,
+and the weights (11.3 GB) exceed the 256 MB last-level cache, so every call
+streams them from HBM.
 
-Prints one JSON line.  value = tokens per second over the step.
+Sections (--sections, default all of them):
+  layer    the headline step: plain moe_fp8_forward calls timed over exactly
+           --steps steps (value, ms_per_step, per-phase median / p10 / p90),
+           then a second pass through moe_fp8_forward_traced, whose HIP events
+           on the launch stream give every stage's time, the dominant kernel
+           and its roofline;
+  configs  every other workload as its own line: tiny T=16, Mixtral-shaped
+           T=64 / 512, Qwen3-shaped T=1 / 32 / 4096 (twelve rotating weight
+           replicas, so the experts a small batch touches never sit in the
+           last-level cache); tokens/s, both roofline fractions, the target;
+  quant    the standalone activation quantiser on bf16 [16384, 7168] with 1%
+           x100 outliers (three rotating inputs), block and MXFP8 scales;
+  linear   the dense block-FP8 and MXFP8 linears on a DeepSeek-V3-shaped down
+           projection (7168 x 18432) at M = 64 and 8192;
+  batched  the batched (masked) expert format;
+  mx       the MXFP8 layer on the headline inputs;
+  peaks    what the part sustains: a read-only HBM stream, a device copy and
+           register-only MFMA chains of both GEMMs' instruction types.
+
+Prints one JSON line.  value = tokens per second over the headline step.
 """
 
 import argparse
@@ -30,14 +48,18 @@ METRIC = "fused FP8 MoE tokens/s + % of HBM/MFMA roofline, decode M=64 & prefill
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_FP8_PEAK = 5.0e15     # dense FP8 FLOP/s
 MFMA_F16_PEAK = 2.5e15     # dense f16 / bf16 FLOP/s
-# MFMA type of each contraction: GEMM1 runs on f16 MFMAs of exactly converted
-# e4m3 operands, GEMM2 on FP8 MFMAs
-STAGE_PEAK = {"gemm1": MFMA_F16_PEAK, "gemm2": MFMA_FP8_PEAK}
+SECTIONS = ["layer", "configs", "quant", "linear", "batched", "mx", "peaks"]
+# targets of the configurations: decode batches >= 60% of the HBM roofline,
+# prefill batches >= 50% of the dense-FP8 MFMA peak (a Mixtral-shaped T=512
+# batch stays below the ridge even at peak and is held to the HBM target)
+TARGETS = {("tiny", 16): None, ("mixtral", 64): ("hbm", 0.6), ("mixtral", 512): ("hbm", 0.6),
+           ("dsv3", 64): ("hbm", 0.6), ("dsv3", 8192): ("mfma", 0.5),
+           ("qwen3", 1): ("hbm", 0.6), ("qwen3", 32): ("hbm", 0.6), ("qwen3", 4096): ("mfma", 0.5)}
 
 # HBM bytes per launch of the two GEMMs, from rocprofv3 FETCH_SIZE (x2) and
 # WRITE_SIZE (x1) passes, each scaled by what the same counter reads for a
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
-# kernel source they were taken on: bench reports null traffic once
+# kernel source they were taken on: the line reports null traffic once
 # gemm.hip differs from this hash.
 TRAFFIC_SOURCE_SHA256 = "c57127a888b3849badba0b4dbc0ef443f82969b6c542f60ea5be158607bd4216"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
@@ -48,7 +70,7 @@ TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
 }
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
@@ -56,15 +78,20 @@ def parse():
     p.add_argument("--workload", default="dsv3", choices=["dsv3", "mixtral", "qwen3", "tiny"])
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
     p.add_argument("--phase", default="both", choices=["both", "decode", "prefill"],
-                   help="time one batch size only (for per-kernel profiles)")
+                   help="headline step with one batch size only (for per-kernel profiles)")
+    p.add_argument("--sections", default=",".join(SECTIONS),
+                   help="comma-separated subset of " + ",".join(SECTIONS))
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--layer-only", action="store_true",
-                   help="time only the MoE layer (skip the standalone quantiser, dense linears, "
-                        "batched experts and MXFP8 layer)")
+    p.add_argument("--layer-only", action="store_true", help="same as --sections layer")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run a plain device-to-device copy of this many MiB (three times), "
                         "the reference kernel that scales the HBM byte counters")
-    return p.parse_args()
+    a = p.parse_args(argv)
+    a.sections = ["layer"] if a.layer_only else [s for s in a.sections.split(",") if s]
+    bad = [s for s in a.sections if s not in SECTIONS]
+    if bad:
+        p.error(f"unknown sections {bad}")
+    return a
 
 
 def batch_sizes(name):
@@ -98,8 +125,18 @@ def algorithmic(ids, T, H, I, E, k):
 
 
 def roofline_of(nbytes, flops, seconds, mfma_peak=MFMA_FP8_PEAK):
+    """Whichever of the HBM and MFMA times is longer at the published peaks
+    bounds the work; achieved rate and fraction of that peak."""
     t_hbm, t_mfma = nbytes / HBM_PEAK, flops / mfma_peak
     if t_mfma > t_hbm:
+        return roofline_at(nbytes, flops, seconds, "mfma", mfma_peak)
+    return roofline_at(nbytes, flops, seconds, "hbm")
+
+
+def roofline_at(nbytes, flops, seconds, bound, mfma_peak=MFMA_FP8_PEAK):
+    """The roofline entry against a given bound: "hbm" (bytes over 8 TB/s) or
+    "mfma" (flops over the given MFMA peak)."""
+    if bound == "mfma":
         a = flops / seconds / 1e12
         return {"bound": "mfma", "achieved": a, "peak": mfma_peak / 1e12, "unit": "TFLOP/s",
                 "frac": a / (mfma_peak / 1e12)}
@@ -108,11 +145,38 @@ def roofline_of(nbytes, flops, seconds, mfma_peak=MFMA_FP8_PEAK):
             "frac": a / (HBM_PEAK / 1e9)}
 
 
+def fractions(nbytes, flops, seconds):
+    """Both fractions of the published roofline, and their maximum (the
+    roofline fraction of the measurement plan: max(B/BW, F/PEAK_FP8) / t)."""
+    h = nbytes / seconds / HBM_PEAK
+    m = flops / seconds / MFMA_FP8_PEAK
+    return {"hbm_frac": h, "mfma_frac": m, "roofline_frac": max(h, m),
+            "bound_at_peak": "mfma" if flops / MFMA_FP8_PEAK > nbytes / HBM_PEAK else "hbm"}
+
+
+def stats(ms):
+    """median, p10, p90 and mean of a list of milliseconds"""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median_ms": float(np.median(a)), "p10_ms": float(np.percentile(a, 10)),
+            "p90_ms": float(np.percentile(a, 90)), "mean_ms": float(a.mean()), "n": int(a.size)}
+
+
+def cpu_threads():
+    """CPU threads the oracle may use: the process's CPU affinity, capped by
+    the thread count the environment grants (OMP_NUM_THREADS, when set)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
 def cpu_baseline(w, x_dec, logits_dec, k, n_tok):
     """The oracle, as it stands, on the first n_tok tokens of the decode batch."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     from oracle import moe as ref_moe
     from oracle import router as ref_router
@@ -127,13 +191,323 @@ def cpu_baseline(w, x_dec, logits_dec, k, n_tok):
     w13[experts] = w["w13"][sel].cpu().numpy()
     w2[experts] = w["w2"][sel].cpu().numpy()
     w13s, w2s = w["w13_scale"].cpu().numpy(), w["w2_scale"].cpu().numpy()
-    t0 = time.perf_counter()
-    ref_moe.moe_forward(x, logits, w13, w13s, w2, w2s, k, True)
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    threads = cpu_threads()
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        ref_moe.moe_forward(x, logits, w13, w13s, w2, w2s, k, True)
+        dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{n_tok} tokens of the T=64 decode batch ({experts.size} experts, "
                       f"{n_tok * k} token-expert pairs), float64 dequantised GEMMs; {dt:.1f} s"}
+
+
+def timed_calls(fn, n, warmup=3):
+    """fn() n times after warmup, each call bracketed by HIP events on the
+    current stream; returns the per-call milliseconds."""
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def run_layer(args, moe, dev, c, w, phases, order):
+    """The headline step: plain forwards timed over exactly args.steps steps,
+    then a traced pass for the stage times."""
+    import numpy as np
+    import torch
+    H, I, E, k = c["H"], c["I"], c["E"], c["top_k"]
+
+    def run(ph, events=None):
+        moe.moe_fp8_forward(ph["x"], ph["logits"], *w, k, True, out=ph["out"], workspace=ph["ws"],
+                            events=events)
+
+    for _ in range(args.warmup):
+        for n in order:
+            run(phases[n])
+    # exactly args.steps steps, plain forwards; events between the phases
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for i, n in enumerate(order):
+            run(phases[n])
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)]
+    phase_ms = {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+                for i, n in enumerate(order)}
+
+    # the same steps through the traced forward: per-stage HIP events on the launch stream
+    nst = len(moe.STAGES)
+    tev = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+               for _ in range(args.steps)] for n in order}
+    for n in order:
+        for lst in tev[n]:
+            for e in lst:
+                e.record()          # creates the HIP events
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        for n in order:
+            run(phases[n], tev[n][s])
+    torch.cuda.synchronize()
+
+    result, kernels = {}, {}
+    for n in order:
+        ph = phases[n]
+        T = ph["T"]
+        taps = moe.workspace_taps(ph["ws"], T, H, I, E, k)
+        alg = algorithmic(taps["topk_ids"].cpu().numpy(), T, H, I, E, k)
+        st = np.array([[tev[n][s][i].elapsed_time(tev[n][s][i + 1]) for i in range(nst)]
+                       for s in range(args.steps)])
+        sm = stats(phase_ms[n])
+        lb, lf = alg["layer_bytes"], alg["layer_flops"]
+        t = sm["median_ms"] * 1e-3
+        tgt = TARGETS.get((args.workload, T))
+        fr = fractions(lb, lf, t)
+        result[n] = {"T": T, **sm, "tokens_per_s": T / t, "active_experts": alg["active_experts"],
+                     "alg_bytes": lb, "alg_flops": lf, **fr,
+                     "target": None if tgt is None else
+                     {"bound": tgt[0], "frac": tgt[1], "met": fr[tgt[0] + "_frac"] >= tgt[1]},
+                     "stage_ms_mean": {s: float(v) for s, v in zip(moe.STAGES, st.mean(axis=0))},
+                     "stage_ms_median": {s: float(v) for s, v in zip(moe.STAGES, np.median(st, axis=0))},
+                     "traced_ms_mean": float(st.sum(axis=1).mean())}
+        for i, s in enumerate(moe.STAGES):
+            b, f = alg["stage"][s]
+            kernels[f"{n}.{s}"] = {"ms": float(st[:, i].mean()), "bytes": b, "flops": f, "phase": n}
+    return {"wall_s": wall, "step_ms": stats(step_ms), "phases": result, "kernels": kernels}
+
+
+def dominant_roofline(kernels, workload, peaks):
+    """Roofline of the kernel with the longest mean launch: a prefill-phase
+    kernel against the dense-FP8 MFMA peak (the bar prefill batches are held
+    to), a decode-phase kernel against the HBM peak."""
+    name = max(kernels, key=lambda s: kernels[s]["ms"])
+    k = kernels[name]
+    bound = "mfma" if k["phase"] == "prefill" and k["flops"] else "hbm"
+    roof = roofline_at(k["bytes"], k["flops"], k["ms"] * 1e-3, bound)
+    if bound == "mfma":
+        roof["frac_of_f16_peak"] = roof["achieved"] / (MFMA_F16_PEAK / 1e12)
+    roof["hbm_frac"] = k["bytes"] / (k["ms"] * 1e-3) / HBM_PEAK
+    if peaks:
+        key = "mfma_fp8_TFLOP_per_s" if bound == "mfma" else "hbm_read_GB_per_s"
+        roof["frac_of_measured_peak"] = roof["achieved"] / peaks[key]
+    traffic = None
+    src = os.path.join(ROOT, "fp8_block_quantized_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as fh:
+        same_source = hashlib.sha256(fh.read()).hexdigest() == TRAFFIC_SOURCE_SHA256
+    if workload == "dsv3" and same_source and name in TRAFFIC:
+        traffic = float(sum(TRAFFIC[name]))
+    roof.update({"kernel": name, "traffic": traffic, "traffic_unit": "bytes per launch",
+                 "alg_bytes_per_launch": k["bytes"], "alg_flops_per_launch": k["flops"],
+                 "ms_per_launch": k["ms"], "timing": "mean of HIP events on the launch stream "
+                                                     "around the kernel, traced pass"})
+    return roof
+
+
+def run_configs(args, moe, dev, skip):
+    """Every other workload and batch size, plain forwards, median / p10 / p90."""
+    import numpy as np
+    import torch
+    from synth import MOE_WORKLOADS, make_activations, make_weights
+    out = {}
+    for name in ("tiny", "mixtral", "qwen3", "dsv3"):
+        c = MOE_WORKLOADS[name]
+        Ts = [T for T in c["T"] if (name, T) not in skip]
+        if not Ts:
+            continue
+        H, I, E, k = c["H"], c["I"], c["E"], c["top_k"]
+        base = 1000 * c["index"]
+        w = make_weights(H, I, E, base + 2, dev)
+        wbytes = sum(t.numel() * t.element_size() for t in w)
+        # replicas so that the weights a call touches are not in the 256 MB
+        # last-level cache when it comes round again (a copy of the whole set
+        # per replica; small-batch calls touch only a few experts of each)
+        nrep = 12 if name == "qwen3" else 1
+        reps = [w] + [tuple(t.clone() for t in w) for _ in range(nrep - 1)]
+        for T in Ts:
+            x, logits = make_activations(H, E, T, base, c["logits"], dev)
+            ws = moe.alloc_workspace(T, H, I, E, k, dev)
+            o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            ms = timed_calls(lambda i: moe.moe_fp8_forward(x, logits, *reps[i % nrep], k, True,
+                                                           out=o, workspace=ws), args.steps)
+            taps = moe.workspace_taps(ws, T, H, I, E, k)
+            alg = algorithmic(taps["topk_ids"].cpu().numpy(), T, H, I, E, k)
+            sm = stats(ms)
+            fr = fractions(alg["layer_bytes"], alg["layer_flops"], sm["median_ms"] * 1e-3)
+            tgt = TARGETS.get((name, T))
+            out[f"{name}.T{T}"] = {
+                "workload": f"{name}-shaped H={H} I={I} E={E} top_k={k}", "T": T,
+                "block_m": taps["block_m"], **sm, "tokens_per_s": T / (sm["median_ms"] * 1e-3),
+                "active_experts": alg["active_experts"], "alg_bytes": alg["layer_bytes"],
+                "alg_flops": alg["layer_flops"], **fr, "weight_replicas": nrep,
+                "weight_bytes_per_replica": wbytes,
+                "target": None if tgt is None else
+                {"bound": tgt[0], "frac": tgt[1], "met": fr[tgt[0] + "_frac"] >= tgt[1]}}
+            del x, logits, ws, o
+        del w, reps
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_quant(args, moe, dev):
+    import numpy as np
+    import torch
+    from synth import QUANT_WORKLOAD, quant_input
+    M, K = QUANT_WORKLOAD["M"], QUANT_WORKLOAD["K"]
+    xq_in = [quant_input(device=dev, seed_base=4000 + 10 * i) for i in range(3)]
+    q_out = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(3)]
+    s_out = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(3)]
+    ms = timed_calls(lambda i: moe.per_token_group_quant_fp8(xq_in[i % 3], q=q_out[i % 3],
+                                                             scales=s_out[i % 3]), args.steps)
+    sm = stats(ms)
+    q_bytes = 2 * M * K + M * K + 4 * M * (K // 128)
+    res = {"M": M, "K": K, **sm, "alg_bytes": q_bytes,
+           "GB_per_s": q_bytes / (sm["median_ms"] * 1e-3) / 1e9,
+           "hbm_frac": q_bytes / (sm["median_ms"] * 1e-3) / HBM_PEAK}
+    e_out = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(3)]
+    ms = timed_calls(lambda i: moe.per_token_group_quant_fp8_fmt(xq_in[i % 3], 32, "ue8m0",
+                                                                 q=q_out[i % 3], scales=e_out[i % 3]),
+                     args.steps)
+    sm = stats(ms)
+    q_bytes = 2 * M * K + M * K + M * (K // 32)
+    res["mxfp8_group32_ue8m0"] = {**sm, "alg_bytes": q_bytes,
+                                  "GB_per_s": q_bytes / (sm["median_ms"] * 1e-3) / 1e9,
+                                  "hbm_frac": q_bytes / (sm["median_ms"] * 1e-3) / HBM_PEAK}
+    return res
+
+
+def run_linear(args, moe, dev):
+    import torch
+    from synth import LINEAR_WORKLOAD, MX_LINEAR_WORKLOAD, make_linear, make_mx_linear
+
+    def time_linear(fn, ws_bytes, make, wl, scale_bytes):
+        LN, LK = wl["N"], wl["K"]
+        res = {"workload": f"DeepSeek-V3-shaped dense down projection N={LN} K={LK}"}
+        for LM in wl["M"]:
+            lx, lw, lws = make(LM, LN, LK, 1000 * wl["index"], device=dev)
+            # three weight replicas in rotation (3 x 132 MB > the 256 MB cache),
+            # so that every call streams its weights from HBM
+            lrep = [(lw, lws)] + [(lw.clone(), lws.clone()) for _ in range(2)]
+            lout = torch.empty((LM, LN), dtype=torch.bfloat16, device=dev)
+            lwsp = torch.empty(ws_bytes(LM, LN, LK), dtype=torch.uint8, device=dev)
+            ms = timed_calls(lambda i: fn(lx, *lrep[i % 3], out=lout, workspace=lwsp), args.steps)
+            sm = stats(ms)
+            lbytes = LN * LK + scale_bytes(LN, LK) + 2 * LM * LK + 2 * LM * LN
+            r = roofline_of(lbytes, 2 * LM * LN * LK, sm["median_ms"] * 1e-3, MFMA_FP8_PEAK)
+            r.update({"M": LM, **sm, "alg_bytes": lbytes, "alg_flops": 2 * LM * LN * LK})
+            res[f"M{LM}"] = r
+            del lx, lw, lws, lrep, lout, lwsp
+        return res
+
+    dense = time_linear(moe.fp8_block_linear, moe.fp8_block_linear_workspace_bytes, make_linear,
+                        LINEAR_WORKLOAD, lambda n, k: 4 * (n // 128) * (k // 128))
+    dense_mx = time_linear(moe.mxfp8_linear, moe.mxfp8_linear_workspace_bytes, make_mx_linear,
+                           MX_LINEAR_WORKLOAD, lambda n, k: n * (k // 32))
+    return dense, dense_mx
+
+
+def run_batched(args, moe, dev):
+    import torch
+    from synth import BATCHED_WORKLOAD as BW
+    from synth import make_weights
+    bE, bM, bH, bI = BW["E"], BW["M"], BW["H"], BW["I"]
+    gb = torch.Generator(device="cpu").manual_seed(1000 * BW["index"] + 1)
+    bcounts = torch.randint(BW["min_count"], bM + 1, (bE,), generator=gb, dtype=torch.int32)
+    bx = torch.randn((bE, bM, bH), generator=torch.Generator(device=dev).manual_seed(1000 * BW["index"]),
+                     device=dev).to(torch.bfloat16)
+    bw = make_weights(bH, bI, bE, 1000 * BW["index"] + 2, dev)
+    bc_dev = bcounts.to(dev)
+    bout = torch.empty_like(bx)
+    bws = torch.empty(moe.moe_fp8_batched_workspace_bytes(bE, bM, bH, bI), dtype=torch.uint8, device=dev)
+    ms = timed_calls(lambda i: moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws),
+                     args.steps)
+    sm = stats(ms)
+    rows = int(bcounts.sum())
+    active = int((bcounts > 0).sum())
+    wbytes = active * (2 * bI * bH + bH * bI + 4 * (2 * bI // 128) * (bH // 128) + 4 * (bH // 128) * (bI // 128))
+    bbytes = wbytes + 2 * rows * bH + 2 * bE * bM * bH
+    bflops = 6 * rows * bH * bI
+    # GEMM1 (4 H I flops per row) runs on f16 MFMAs, GEMM2 (2 H I) on FP8 ones:
+    # the peak of the mix is 6 / (4 / f16 peak + 2 / FP8 peak)
+    blend = 6.0 / (4.0 / MFMA_F16_PEAK + 2.0 / MFMA_FP8_PEAK)
+    batched = roofline_of(bbytes, bflops, sm["median_ms"] * 1e-3, blend)
+    batched.update({"workload": f"DeepSeek-V3-shaped experts of one rank of eight: E={bE} max_tokens={bM} "
+                                f"H={bH} I={bI}, counts uniform in [{BW['min_count']}, {bM}]",
+                    "rows": rows, **sm, "alg_bytes": bbytes, "alg_flops": bflops,
+                    "hbm_frac": bbytes / (sm["median_ms"] * 1e-3) / HBM_PEAK})
+    return batched
+
+
+def run_mx(args, moe, dev, c, phases, order):
+    import numpy as np
+    import torch
+    from synth import make_mx_weights
+    H, I, E, k = c["H"], c["I"], c["E"], c["top_k"]
+    mxw = make_mx_weights(H, I, E, 1000 * c["index"] + 2, dev)
+    res = {"workload": f"{args.workload}-shaped MoE layer with MXFP8 weights and activations"}
+    for n in order:
+        ph = phases[n]
+        T = ph["T"]
+        mws = torch.empty(moe.moe_fp8_mx_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
+        ms = timed_calls(lambda i: moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True,
+                                                          out=ph["out"], workspace=mws), args.steps)
+        sm = stats(ms)
+        ids = moe.workspace_taps(mws, T, H, I, E, k, mx=True)["topk_ids"].cpu().numpy()
+        e_act = int(np.unique(ids).size)
+        mbytes = e_act * (2 * I * H + H * I) * 33 // 32 + 4 * T * H
+        mflops = 6 * T * k * H * I
+        r = roofline_of(mbytes, mflops, sm["median_ms"] * 1e-3, MFMA_FP8_PEAK)
+        r.update({"T": T, **sm, "tokens_per_s": T / (sm["median_ms"] * 1e-3), "active_experts": e_act,
+                  "alg_bytes": mbytes, "alg_flops": mflops,
+                  **fractions(mbytes, mflops, sm["median_ms"] * 1e-3)})
+        res[n] = r
+        del mws
+    del mxw
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_peaks(args, moe, dev):
+    """What the part sustains: a read-only stream of 4 GiB (the weight-streaming
+    decode GEMMs' bound), a 1 GiB device copy (read + write) and register-only
+    MFMA chains of the two GEMMs' instruction types."""
+    import torch
+    nb = 4 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    nblk = 2048              # eight 16-byte loads in flight per thread: 7.0 TB/s on the box
+    sink = torch.empty(nblk * 256, dtype=torch.int32, device=dev)
+    ms = timed_calls(lambda i: moe.moe_hbm_read_probe(src, nblk, sink), 5, warmup=2)
+    peaks = {"hbm_read_GB_per_s": nb / (min(ms) * 1e-3) / 1e9}
+    del src, sink
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    ms = timed_calls(lambda i: dst.copy_(src), 5, warmup=2)
+    peaks["hbm_copy_GB_per_s"] = 2 * nb / (min(ms) * 1e-3) / 1e9
+    del src, dst
+    nblk = 2048
+    sink = torch.empty(nblk * 256, dtype=torch.float32, device=dev)
+    for kind, iters in (("f16", 5000), ("fp8", 2500)):
+        fl = [0]
+
+        def go(i):
+            fl[0] = moe.moe_mfma_rate_probe(kind, iters, nblk, sink)
+        ms = timed_calls(go, 3, warmup=1)
+        peaks[f"mfma_{kind}_TFLOP_per_s"] = fl[0] / (min(ms) * 1e-3) / 1e12
+    del sink
+    return peaks
 
 
 def main():
@@ -142,11 +516,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is built and measured on a single MI355X)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     import fp8_block_quantized_amd as moe
-    from synth import MOE_WORKLOADS, make_activations, make_weights, quant_input
+    from synth import MOE_WORKLOADS, make_activations, make_weights
 
     moe.load_library()
     dev = torch.device("cuda:0")
@@ -155,8 +528,7 @@ def main():
     H, I, E, k = c["H"], c["I"], c["E"], c["top_k"]
     base = 1000 * c["index"]
     T_dec, T_pre = batch_sizes(args.workload)
-    w13, w13s, w2, w2s = make_weights(H, I, E, base + 2, dev)
-    wts = {"w13": w13, "w13_scale": w13s, "w2": w2, "w2_scale": w2s}
+    w = make_weights(H, I, E, base + 2, dev)
     phases = {}
     for name, T in (("decode", T_dec), ("prefill", T_pre)):
         if args.phase not in ("both", name):
@@ -169,53 +541,24 @@ def main():
     if args.phase != "both":
         order = [args.phase]
 
-    def run(ph, events=None):
-        moe.moe_fp8_forward(ph["x"], ph["logits"], w13, w13s, w2, w2s, k, True,
-                            out=ph["out"], workspace=ph["ws"], events=events)
-
-    for _ in range(args.warmup):
-        for n in order:
-            run(phases[n])
-    torch.cuda.synchronize()
-
-    nst = len(moe.STAGES)
-    evs = {n: [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
-               for _ in range(args.steps)] for n in order}
-    for n in order:
-        for lst in evs[n]:
-            for e in lst:
-                e.record()          # creates the HIP events
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        for n in order:
-            run(phases[n], evs[n][s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    result_phases = {}
-    kernels = {}
-    for n in order:
-        ph = phases[n]
-        T = ph["T"]
-        taps = moe.workspace_taps(ph["ws"], T, H, I, E, k)
-        alg = algorithmic(taps["topk_ids"].cpu().numpy(), T, H, I, E, k)
-        st_ms = np.array([[evs[n][s][i].elapsed_time(evs[n][s][i + 1]) for i in range(nst)]
-                          for s in range(args.steps)]).mean(axis=0)
-        layer_ms = float(st_ms.sum())
-        lb, lf = alg["layer_bytes"], alg["layer_flops"]
-        result_phases[n] = {
-            "T": T, "ms": layer_ms, "tokens_per_s": T / (layer_ms * 1e-3),
-            "active_experts": alg["active_experts"],
-            "alg_bytes": lb, "alg_flops": lf,
-            "hbm_frac": lb / (layer_ms * 1e-3) / HBM_PEAK,
-            "mfma_frac": lf / (layer_ms * 1e-3) / MFMA_FP8_PEAK,
-            "stage_ms": {s: float(v) for s, v in zip(moe.STAGES, st_ms)},
-        }
-        for s, v in zip(moe.STAGES, st_ms):
-            b, f = alg["stage"][s]
-            kernels[f"{n}.{s}"] = {"ms": float(v), "bytes": b, "flops": f,
-                                   "peak": STAGE_PEAK.get(s, MFMA_FP8_PEAK)}
+    out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8e4m3 (GEMM2 FP8 MFMA, f32 acc; GEMM1 exact f16 MFMA, f64 acc at decode, "
+                    "f32 at prefill; bf16 in/out)",
+           "data": "synthetic",
+           "config": {"workload": f"{args.workload}-shaped MoE layer H={H} I={I} E={E} top_k={k}, "
+                                  + " + ".join(f"{n} T={phases[n]['T']}" for n in order) + " per step",
+                      "H": H, "I": I, "E": E, "top_k": k, "T": {n: phases[n]["T"] for n in order},
+                      "block_m": {n: moe.moe_fp8_block_m(phases[n]["T"], H, I, E, k) for n in order}}}
+    layer = None
+    if "layer" in args.sections:
+        layer = run_layer(args, moe, dev, c, w, phases, order)
+        tokens = sum(phases[n]["T"] for n in order)
+        out["value"] = tokens / (layer["wall_s"] / args.steps)
+        out["ms_per_step"] = layer["wall_s"] / args.steps * 1e3
+        out["step_ms"] = layer["step_ms"]
+        out["phases"] = layer["phases"]
 
     if args.copy_calibration_mib:
         nb = args.copy_calibration_mib << 20
@@ -227,221 +570,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def extras():
-        """The timed sections after the layer: standalone quantiser, dense
-        linears, batched experts and the MXFP8 layer."""
-        # standalone activation quantiser, rotating three input buffers (> MALL)
-        from synth import QUANT_WORKLOAD
-        M, K = QUANT_WORKLOAD["M"], QUANT_WORKLOAD["K"]
-        xq_in = [quant_input(device=dev, seed_base=4000 + 10 * i) for i in range(3)]
-        q_out = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(3)]
-        s_out = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(3)]
-        for i in range(3):
-            moe.per_token_group_quant_fp8(xq_in[i], q=q_out[i], scales=s_out[i])
-        qe = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-        torch.cuda.synchronize()
-        for s in range(args.steps):
-            qe[2 * s].record()
-            moe.per_token_group_quant_fp8(xq_in[s % 3], q=q_out[s % 3], scales=s_out[s % 3])
-            qe[2 * s + 1].record()
-        torch.cuda.synchronize()
-        q_ms = float(np.mean([qe[2 * s].elapsed_time(qe[2 * s + 1]) for s in range(args.steps)]))
-        q_bytes = 2 * M * K + M * K + 4 * M * (K // 128)
-        quant = {"M": M, "K": K, "ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
-                 "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
+    if "configs" in args.sections:
+        out["configs"] = run_configs(args, moe, dev, skip={(args.workload, T) for T in (T_dec, T_pre)}
+                                     if layer else set())
+    if "quant" in args.sections:
+        out["quant_standalone"] = run_quant(args, moe, dev)
+    if "linear" in args.sections:
+        out["dense_linear"], out["dense_linear_mxfp8"] = run_linear(args, moe, dev)
+    if "batched" in args.sections:
+        out["batched_experts"] = run_batched(args, moe, dev)
+    if "mx" in args.sections:
+        out["moe_mxfp8"] = run_mx(args, moe, dev, c, phases, order)
+    peaks = run_peaks(args, moe, dev) if "peaks" in args.sections else None
+    out["measured_peaks"] = peaks
+    out["roofline"] = dominant_roofline(layer["kernels"], args.workload, peaks) if layer else None
+    out["kernels"] = layer["kernels"] if layer else None
 
-        # the same quantiser with MXFP8 scales: groups of 32, UE8M0 exponent bytes
-        e_out = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(3)]
-        for i in range(3):
-            moe.per_token_group_quant_fp8_fmt(xq_in[i], 32, "ue8m0", q=q_out[i], scales=e_out[i])
-        torch.cuda.synchronize()
-        for s in range(args.steps):
-            qe[2 * s].record()
-            moe.per_token_group_quant_fp8_fmt(xq_in[s % 3], 32, "ue8m0", q=q_out[s % 3], scales=e_out[s % 3])
-            qe[2 * s + 1].record()
-        torch.cuda.synchronize()
-        q_ms = float(np.mean([qe[2 * s].elapsed_time(qe[2 * s + 1]) for s in range(args.steps)]))
-        q_bytes = 2 * M * K + M * K + M * (K // 32)
-        quant["mxfp8_group32_ue8m0"] = {"ms": q_ms, "GB_per_s": q_bytes / (q_ms * 1e-3) / 1e9,
-                                        "hbm_frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK}
-        del xq_in, q_out, s_out, e_out
-
-        # dense linears (the layer's E = 1 neighbour), decode and prefill batches:
-        # block FP8 (128x128 weight blocks, float32 scales) and MXFP8 ([1, 32], UE8M0)
-        from synth import LINEAR_WORKLOAD, MX_LINEAR_WORKLOAD, make_linear, make_mx_linear
-
-        def time_linear(fn, ws_bytes, make, wl, scale_bytes):
-            LN, LK = wl["N"], wl["K"]
-            res = {"workload": f"DeepSeek-V3-shaped dense down projection N={LN} K={LK}"}
-            for LM in wl["M"]:
-                lx, lw, lws = make(LM, LN, LK, 1000 * wl["index"], device=dev)
-                # three weight replicas in rotation (3 x 132 MB > the 256 MB MALL),
-                # so that every call streams its weights from HBM
-                lrep = [(lw, lws)] + [(lw.clone(), lws.clone()) for _ in range(2)]
-                lout = torch.empty((LM, LN), dtype=torch.bfloat16, device=dev)
-                lwsp = torch.empty(ws_bytes(LM, LN, LK), dtype=torch.uint8, device=dev)
-                for i in range(3):
-                    fn(lx, *lrep[i], out=lout, workspace=lwsp)
-                le = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                torch.cuda.synchronize()
-                le[0].record()
-                for i in range(args.steps):
-                    fn(lx, *lrep[i % 3], out=lout, workspace=lwsp)
-                le[1].record()
-                torch.cuda.synchronize()
-                lms = le[0].elapsed_time(le[1]) / args.steps
-                lbytes = LN * LK + scale_bytes(LN, LK) + 2 * LM * LK + 2 * LM * LN
-                r = roofline_of(lbytes, 2 * LM * LN * LK, lms * 1e-3, MFMA_FP8_PEAK)
-                r.update({"M": LM, "ms": lms, "alg_bytes": lbytes, "alg_flops": 2 * LM * LN * LK})
-                res[f"M{LM}"] = r
-                del lx, lw, lws, lrep, lout, lwsp
-            return res
-
-        dense = time_linear(moe.fp8_block_linear, moe.fp8_block_linear_workspace_bytes, make_linear,
-                            LINEAR_WORKLOAD, lambda n, k: 4 * (n // 128) * (k // 128))
-        dense_mx = time_linear(moe.mxfp8_linear, moe.mxfp8_linear_workspace_bytes, make_mx_linear,
-                               MX_LINEAR_WORKLOAD, lambda n, k: n * (k // 32))
-
-        # batched (masked) expert format: one rank's experts, device-side counts
-        from synth import BATCHED_WORKLOAD as BW
-        bE, bM, bH, bI = BW["E"], BW["M"], BW["H"], BW["I"]
-        gb = torch.Generator(device="cpu").manual_seed(1000 * BW["index"] + 1)
-        bcounts = torch.randint(BW["min_count"], bM + 1, (bE,), generator=gb, dtype=torch.int32)
-        bx = torch.randn((bE, bM, bH), generator=torch.Generator(device=dev).manual_seed(1000 * BW["index"]),
-                         device=dev).to(torch.bfloat16)
-        bw = make_weights(bH, bI, bE, 1000 * BW["index"] + 2, dev)
-        bc_dev = bcounts.to(dev)
-        bout = torch.empty_like(bx)
-        bws = torch.empty(moe.moe_fp8_batched_workspace_bytes(bE, bM, bH, bI), dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws)
-        be = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        be[0].record()
-        for _ in range(args.steps):
-            moe.moe_fp8_batched_experts(bx, bc_dev, *bw, out=bout, workspace=bws)
-        be[1].record()
-        torch.cuda.synchronize()
-        bms = be[0].elapsed_time(be[1]) / args.steps
-        rows = int(bcounts.sum())
-        active = int((bcounts > 0).sum())
-        wbytes = active * (2 * bI * bH + bH * bI + 4 * (2 * bI // 128) * (bH // 128) + 4 * (bH // 128) * (bI // 128))
-        bbytes = wbytes + 2 * rows * bH + 2 * bE * bM * bH
-        bflops = 6 * rows * bH * bI
-        # GEMM1 (4 H I flops per row) runs on f16 MFMAs, GEMM2 (2 H I) on FP8 ones:
-        # the peak of the mix is 6 / (4 / f16 peak + 2 / FP8 peak)
-        blend = 6.0 / (4.0 / MFMA_F16_PEAK + 2.0 / MFMA_FP8_PEAK)
-        batched = roofline_of(bbytes, bflops, bms * 1e-3, blend)
-        batched.update({"workload": f"DeepSeek-V3-shaped experts of one rank of eight: E={bE} max_tokens={bM} "
-                                    f"H={bH} I={bI}, counts uniform in [{BW['min_count']}, {bM}]",
-                        "rows": rows, "ms": bms, "alg_bytes": bbytes, "alg_flops": bflops})
-        del bx, bw, bout, bws
-
-        # the MXFP8 layer ([1, 32] blocks, UE8M0 scales, FP8 MFMAs in both GEMMs)
-        # on the same inputs, with the same weights cast to MXFP8
-        from synth import make_mx_weights
-        mxw = make_mx_weights(H, I, E, base + 2, dev)
-        mx_layer = {"workload": f"{args.workload}-shaped MoE layer with MXFP8 weights and activations"}
-        for n in order:
-            ph = phases[n]
-            T = ph["T"]
-            mws = torch.empty(moe.moe_fp8_mx_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
-            for _ in range(3):
-                moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True, out=ph["out"], workspace=mws)
-            me = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            torch.cuda.synchronize()
-            me[0].record()
-            for _ in range(args.steps):
-                moe.moe_fp8_mx_forward(ph["x"], ph["logits"], *mxw, k, True, out=ph["out"], workspace=mws)
-            me[1].record()
-            torch.cuda.synchronize()
-            mms = me[0].elapsed_time(me[1]) / args.steps
-            ids = moe.workspace_taps(mws, T, H, I, E, k, mx=True)["topk_ids"].cpu().numpy()
-            e_act = int(np.unique(ids).size)
-            mbytes = e_act * (2 * I * H + H * I) * 33 // 32 + 4 * T * H
-            mflops = 6 * T * k * H * I
-            r = roofline_of(mbytes, mflops, mms * 1e-3, MFMA_FP8_PEAK)
-            r.update({"T": T, "ms": mms, "tokens_per_s": T / (mms * 1e-3), "active_experts": e_act,
-                      "alg_bytes": mbytes, "alg_flops": mflops})
-            mx_layer[n] = r
-            del mws
-        del mxw
-        # what this part sustains: a plain 1 GiB device copy (read + write) and
-        # register-only MFMA chains of the two GEMMs' instruction types
-        nb = 1 << 30
-        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        copy_ms = []
-        for _ in range(5):
-            ce[0].record()
-            dst.copy_(src)
-            ce[1].record()
-            torch.cuda.synchronize()
-            copy_ms.append(ce[0].elapsed_time(ce[1]))
-        del src, dst
-        nblk = 2048
-        sink = torch.empty(nblk * 256, dtype=torch.float32, device=dev)
-        peaks = {"hbm_copy_GB_per_s": 2 * nb / (min(copy_ms) * 1e-3) / 1e9}
-        for kind, iters in (("f16", 5000), ("fp8", 2500)):
-            moe.moe_mfma_rate_probe(kind, 100, nblk, sink)
-            torch.cuda.synchronize()
-            ce[0].record()
-            fl = moe.moe_mfma_rate_probe(kind, iters, nblk, sink)
-            ce[1].record()
-            torch.cuda.synchronize()
-            peaks[f"mfma_{kind}_TFLOP_per_s"] = fl / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e12
-        del sink
-        return quant, dense, dense_mx, batched, mx_layer, peaks
-
-    if args.layer_only:
-        quant = dense = dense_mx = batched = mx_layer = peaks = None
-    else:
-        quant, dense, dense_mx, batched, mx_layer, peaks = extras()
-
-    dom_name = max(kernels, key=lambda s: kernels[s]["ms"])
-    dom = kernels[dom_name]
-    roof = roofline_of(dom["bytes"], dom["flops"], dom["ms"] * 1e-3, dom["peak"])
-    traffic = None
-    src = os.path.join(ROOT, "fp8_block_quantized_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as fh:
-        same_source = hashlib.sha256(fh.read()).hexdigest() == TRAFFIC_SOURCE_SHA256
-    if args.workload == "dsv3" and same_source and dom_name in TRAFFIC:
-        traffic = float(sum(TRAFFIC[dom_name]))
-    if peaks:
-        key = {"GB/s": "hbm_copy_GB_per_s"}.get(roof["unit"],
-                                              "mfma_f16_TFLOP_per_s" if dom["peak"] == MFMA_F16_PEAK
-                                              else "mfma_fp8_TFLOP_per_s")
-        roof["frac_of_measured_peak"] = roof["achieved"] / peaks[key]
-    roof.update({"kernel": dom_name, "traffic": traffic, "traffic_unit": "bytes per launch",
-                 "alg_bytes_per_launch": dom["bytes"], "alg_flops_per_launch": dom["flops"],
-                 "ms_per_launch": dom["ms"]})
-
-    tokens = sum(phases[n]["T"] for n in order)
-    ms_step = wall / args.steps * 1e3
-    out = {
-        "metric": METRIC, "value": tokens / (wall / args.steps), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8e4m3 (GEMM2 FP8 MFMA, f32 acc; GEMM1 exact f16 MFMA, f64 acc at decode, "
-                 "f32 at prefill; bf16 in/out)",
-        "data": "synthetic",
-        "config": {"workload": f"{args.workload}-shaped MoE layer H={H} I={I} E={E} top_k={k}, "
-                               + " + ".join(f"{n} T={phases[n]['T']}" for n in order) + " per step",
-                   "H": H, "I": I, "E": E, "top_k": k, "T": {n: phases[n]["T"] for n in order},
-                   "block_m": {n: moe.moe_fp8_block_m(phases[n]["T"], H, I, E, k) for n in order}},
-        "roofline": roof,
-        "phases": result_phases,
-        "quant_standalone": quant,
-        "dense_linear": dense,
-        "dense_linear_mxfp8": dense_mx,
-        "batched_experts": batched,
-        "moe_mxfp8": mx_layer,
-        "measured_peaks": peaks,
-    }
-    if not args.no_cpu_baseline and "decode" in phases:
+    if layer and not args.no_cpu_baseline and "decode" in phases:
         ph = phases["decode"]
-        out["cpu_baseline"] = cpu_baseline(wts, ph["x"], ph["logits"], k, args.cpu_sample_tokens)
+        wd = dict(zip(("w13", "w13_scale", "w2", "w2_scale"), w))
+        out["cpu_baseline"] = cpu_baseline(wd, ph["x"], ph["logits"], k, args.cpu_sample_tokens)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))

@@ -34,7 +34,8 @@ EXPORTS = ["moe_fp8_block_m", "moe_fp8_workspace_bytes", "moe_fp8_workspace_layo
            "moe_align_scratch_bytes", "moe_align", "moe_align_noalloc",
            "moe_align_noalloc_max_scratch_bytes", "moe_status_string",
            "fp8_block_linear_workspace_bytes", "fp8_block_linear",
-           "mxfp8_linear_workspace_bytes", "mxfp8_linear", "moe_mfma_rate_probe"]
+           "mxfp8_linear_workspace_bytes", "mxfp8_linear", "moe_mfma_rate_probe",
+           "moe_hbm_read_probe"]
 
 
 class MoeError(RuntimeError):
@@ -106,6 +107,8 @@ def load_library(path=LIB_PATH):
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_mfma_rate_probe.argtypes = [c_int, c_int, c_int, vp, vp]
     lib.moe_mfma_rate_probe.restype = c_int
+    lib.moe_hbm_read_probe.argtypes = [vp, c_size, c_int, vp, vp]
+    lib.moe_hbm_read_probe.restype = c_int
     _lib = lib
     return lib
 
@@ -597,3 +600,17 @@ def moe_mfma_rate_probe(kind, iters, nblocks, sink, stream=None):
     _check("moe_mfma_rate_probe", st)
     return nblocks * 4 * iters * 8 * MFMA_PROBE_FLOPS[kind]
 
+
+def moe_hbm_read_probe(src, nblocks, sink, stream=None):
+    """HBM read-stream probe: reads the bytes of the contiguous GPU tensor src
+    once (its size a multiple of 16 bytes); sink is an int32 device tensor of
+    nblocks * 256 that receives one XOR word per thread.  Returns the bytes read."""
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise TypeError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() < nblocks * 256:
+        raise ValueError("sink needs nblocks * 256 words")
+    st = load_library().moe_hbm_read_probe(ctypes.c_void_p(src.data_ptr()), nbytes, int(nblocks),
+                                           _dev(sink, torch.int32, "sink"), _stream(stream))
+    _check("moe_hbm_read_probe", st)
+    return nbytes

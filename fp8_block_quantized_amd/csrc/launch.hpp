@@ -88,5 +88,9 @@ hipError_t launch_combine_slices(const float* part, int y_stride, int nslice, in
 // matrix-core rate probe (kind 0: f16 16x16x32, 1: FP8 16x16x128), nblocks x 256
 // threads, one float per thread stored to sink
 hipError_t launch_mfma_probe(int kind, int iters, int nblocks, float* sink, hipStream_t stream);
+// HBM read-stream probe: nblocks x 256 threads XOR src (bytes, a multiple of
+// 16) into one word per thread of sink
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, int nblocks, uint32_t* sink,
+                                 hipStream_t stream);
 
 }  // namespace moe

@@ -757,4 +757,12 @@ int moe_mfma_rate_probe(int kind, int iters, int nblocks, float* sink, hipStream
   return moe::launch_mfma_probe(kind, iters, nblocks, sink, stream) ? MOE_ERR_HIP : MOE_OK;
 }
 
+int moe_hbm_read_probe(const void* src, size_t bytes, int nblocks, uint32_t* sink,
+                       hipStream_t stream) {
+  if (bytes == 0 || bytes % 16 || nblocks < 1 || nblocks > (1 << 20)) return MOE_ERR_SHAPE;
+  if (!src || !sink) return MOE_ERR_NULL;
+  if ((uintptr_t)src % 16 || (uintptr_t)sink % 4) return MOE_ERR_UNSUPPORTED;
+  return moe::launch_hbm_read_probe(src, bytes, nblocks, sink, stream) ? MOE_ERR_HIP : MOE_OK;
+}
+
 }  // extern "C"

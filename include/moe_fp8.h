@@ -456,6 +456,22 @@ int mxfp8_linear(const void* x, const uint8_t* w, const uint8_t* w_scale, int M,
  */
 int moe_mfma_rate_probe(int kind, int iters, int nblocks, float* sink, hipStream_t stream);
 
+/*
+ * HBM read-stream probe, a measurement aid (not a step of the layer): the
+ * decode-sized GEMMs stream their weights and write almost nothing, so the
+ * rate HBM delivers to a pure read stream is the ceiling they are measured
+ * against beside the published 8 TB/s.  nblocks workgroups of 256 threads
+ * read src (bytes, a multiple of 16; 16-byte aligned) once in a grid-stride
+ * loop of 16-byte loads and store the XOR of each thread's 32-bit words to
+ * sink[thread] (uint32 [nblocks * 256], device, 4-byte aligned, caller-owned):
+ * the XOR of all of sink equals the XOR of all 32-bit words of src.
+ * Returns MOE_OK, MOE_ERR_SHAPE (bytes 0 or not a multiple of 16, nblocks
+ * outside [1, 2^20]), MOE_ERR_NULL, MOE_ERR_UNSUPPORTED (misaligned) or
+ * MOE_ERR_HIP.
+ */
+int moe_hbm_read_probe(const void* src, size_t bytes, int nblocks, uint32_t* sink,
+                       hipStream_t stream);
+
 /* Static description of a moe_status code. */
 const char* moe_status_string(int status);
 

@@ -323,3 +323,12 @@ def test_noalloc_align_scratch_limit_and_argument_checks():
     assert lib.moe_align_noalloc(*ok[:5], None, *ok[6:]) == -1
     assert lib.moe_status_string(-7) != b"unknown status"
 
+
+def test_hbm_read_probe_argument_checks():
+    lib = moe.load_library()
+    vp = ctypes.c_void_p
+    assert lib.moe_hbm_read_probe(vp(4096), 0, 8, vp(4096), None) == -2
+    assert lib.moe_hbm_read_probe(vp(4096), 100, 8, vp(4096), None) == -2
+    assert lib.moe_hbm_read_probe(vp(4096), 4096, 0, vp(4096), None) == -2
+    assert lib.moe_hbm_read_probe(None, 4096, 8, vp(4096), None) == -1
+    assert lib.moe_hbm_read_probe(vp(4100), 4096, 8, vp(4096), None) == -3

@@ -46,3 +46,46 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_roofline_at_a_given_bound():
+    r = bench.roofline_at(1e9, 1e12, 1e-3, "mfma")
+    assert r["peak"] == 5000.0 and abs(r["frac"] - 0.2) < 1e-12
+    r = bench.roofline_at(4e9, 1e12, 1e-3, "hbm")
+    assert r["unit"] == "GB/s" and abs(r["frac"] - 0.5) < 1e-12
+
+
+def test_fractions_take_the_larger_of_the_two_bounds():
+    f = bench.fractions(4e9, 1e12, 1e-3)          # 0.5 of HBM, 0.2 of FP8 MFMA
+    assert abs(f["hbm_frac"] - 0.5) < 1e-12 and abs(f["mfma_frac"] - 0.2) < 1e-12
+    assert abs(f["roofline_frac"] - 0.5) < 1e-12 and f["bound_at_peak"] == "hbm"
+    assert bench.fractions(1e9, 1e12, 1e-3)["bound_at_peak"] == "mfma"
+
+
+def test_stats_median_and_percentiles():
+    s = bench.stats([float(i) for i in range(1, 12)])     # 1 .. 11
+    assert s["median_ms"] == 6.0 and s["n"] == 11
+    assert abs(s["p10_ms"] - 2.0) < 1e-12 and abs(s["p90_ms"] - 10.0) < 1e-12
+
+
+def test_dominant_kernel_bound_follows_its_phase():
+    kernels = {"prefill.gemm1": {"ms": 4.0, "bytes": 8e9, "flops": 4e12, "phase": "prefill"},
+               "decode.gemm1": {"ms": 1.0, "bytes": 5e9, "flops": 1e10, "phase": "decode"}}
+    r = bench.dominant_roofline(kernels, "tiny", None)
+    # prefill: against the dense-FP8 peak even though the bytes take longer at peak
+    assert r["kernel"] == "prefill.gemm1" and r["bound"] == "mfma" and r["peak"] == 5000.0
+    assert abs(r["frac"] - 0.2) < 1e-12 and abs(r["frac_of_f16_peak"] - 0.4) < 1e-12
+    assert r["traffic"] is None
+    kernels["decode.gemm1"]["ms"] = 5.0
+    r = bench.dominant_roofline(kernels, "tiny", {"hbm_read_GB_per_s": 6000.0})
+    assert r["bound"] == "hbm" and abs(r["achieved"] - 1000.0) < 1e-9
+    assert abs(r["frac_of_measured_peak"] - 1000.0 / 6000.0) < 1e-12
+
+
+def test_sections_and_cpu_threads():
+    a = bench.parse(["--sections", "layer,peaks"])
+    assert a.sections == ["layer", "peaks"]
+    assert bench.parse(["--layer-only"]).sections == ["layer"]
+    assert bench.parse([]).sections == bench.SECTIONS
+    n = bench.cpu_threads()
+    assert 1 <= n <= len(os.sched_getaffinity(0))

@@ -49,3 +49,19 @@ def test_probe_closed_form(kind):
     # the FP8 instruction's own accumulation is held to 1e-6
     rtol = 0.0 if kind == "f16" else 1e-6
     np.testing.assert_allclose(waves, want, rtol=rtol, atol=0)
+
+
+def test_hbm_read_probe_reads_every_word():
+    """The XOR of the probe's per-thread words is the XOR of every 32-bit word
+    of the buffer, over a grid that leaves a ragged tail of 16-byte words."""
+    note("hbm read probe")
+    g = torch.Generator().manual_seed(5)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, ((1 << 20) + 36,), generator=g, dtype=torch.int32)
+    nblocks = 7
+    sink = torch.zeros(nblocks * 256, dtype=torch.int32, device="cuda")
+    n = moe.moe_hbm_read_probe(src.cuda(), nblocks, sink)
+    torch.cuda.synchronize()
+    assert n == src.numel() * 4
+    want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
