@@ -528,10 +528,12 @@ def main():
     H, I, E, k = c["H"], c["I"], c["E"], c["top_k"]
     base = 1000 * c["index"]
     T_dec, T_pre = batch_sizes(args.workload)
-    w = make_weights(H, I, E, base + 2, dev)
+    # the headline weights and batches, for the sections that run on them
+    need_layer = "layer" in args.sections or "mx" in args.sections
+    w = make_weights(H, I, E, base + 2, dev) if "layer" in args.sections else None
     phases = {}
     for name, T in (("decode", T_dec), ("prefill", T_pre)):
-        if args.phase not in ("both", name):
+        if args.phase not in ("both", name) or not need_layer:
             continue
         x, logits = make_activations(H, E, T, base, c["logits"], dev)
         phases[name] = {"T": T, "x": x, "logits": logits,
@@ -540,6 +542,7 @@ def main():
     order = ["decode", "prefill"] if T_dec != T_pre else ["decode"]
     if args.phase != "both":
         order = [args.phase]
+    order = [n for n in order if n in phases]
 
     out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
@@ -550,7 +553,8 @@ def main():
            "config": {"workload": f"{args.workload}-shaped MoE layer H={H} I={I} E={E} top_k={k}, "
                                   + " + ".join(f"{n} T={phases[n]['T']}" for n in order) + " per step",
                       "H": H, "I": I, "E": E, "top_k": k, "T": {n: phases[n]["T"] for n in order},
-                      "block_m": {n: moe.moe_fp8_block_m(phases[n]["T"], H, I, E, k) for n in order}}}
+                      "block_m": {n: moe.moe_fp8_block_m(phases[n]["T"], H, I, E, k) for n in order},
+                      "sections": args.sections}}
     layer = None
     if "layer" in args.sections:
         layer = run_layer(args, moe, dev, c, w, phases, order)
