@@ -653,7 +653,9 @@ constexpr int kRingW = 256 * 128;      // 256 weight rows x one 128-byte K block
 //
 // As in GEMM1, a wave whose 64 token rows of the tile are all padding (its
 // first row is the sentinel) loads, waits and stores as usual but skips its
-// MFMAs; its stores write zeros into padding rows, which nothing reads.
+// MFMAs.  The stores of a 16-row group that is all padding go to the 1 KB
+// dump rather than to y: every wave still issues kPf2Stores per tile, which
+// the ring's counted waits rely on, but the padding rows cost no HBM writes.
 constexpr int kPf2Loads = 7;               // DMA instructions per wave per stage
 constexpr int kPf2Stores = 16;             // output stores per wave per tile
 constexpr int kPf2S = 2048;                // token scales, eight 256-byte wave slots
@@ -840,14 +842,16 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
       }
     }
     // y rows of the tile, bf16: kPf2Stores stores whatever the bounds, the
-    // ones outside the stored region (a dense output's ragged edge) into the dump
+    // ones outside the stored region (a dense output's ragged edge) or in an
+    // all-padding 16-row group into the dump
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = cur.b * BM + 64 * wt + 16 * q + l16;
+      const bool pad = load_uniform(args.sorted_ids + cur.b * BM + 64 * wt + 16 * q) >= args.P;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
         const int col = nf + 16 * pp + 4 * g;
-        const bool in = row < args.y_rows && col < args.y_cols;
+        const bool in = !pad && row < args.y_rows && col < args.y_cols;
         if (!kSplitK) {
           uint16_t* dst = in ? args.y_out + (size_t)row * args.y_stride + col : args.y_dump + 4 * lane;
           uint2 v;
@@ -1704,7 +1708,7 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
-                        uint16_t* y, int y_stride, int kslices, float* y_slices,
+                        uint16_t* y, int y_stride, uint16_t* y_dump, int kslices, float* y_slices,
                         hipStream_t stream) {
   if (kslices > 1 && (BM > 64 || !y_slices || kslices > (I >> 7))) return hipErrorInvalidValue;
   GemmArgs a{};
@@ -1713,7 +1717,7 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
   a.act = aq; a.act_scale = as; a.w = w2; a.w_scale = w2s;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
   a.y_out = y; a.y_stride = y_stride;
-  a.y_rows = nblk * BM; a.y_cols = y_stride; a.y_dump = y; a.ksplit = 1;
+  a.y_rows = nblk * BM; a.y_cols = y_stride; a.y_dump = y_dump; a.ksplit = 1;
   a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
   a.n_tiles = (H + 255) / 256; a.nblk = nblk;
   return launch_gemm2_bm(a, BM, stream);
@@ -1722,13 +1726,13 @@ hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, c
 hipError_t launch_gemm2_mx(const uint8_t* aq, const uint8_t* ae, const uint8_t* w2, const uint8_t* w2e,
                            const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                            const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
-                           uint16_t* y, int y_stride, hipStream_t stream) {
+                           uint16_t* y, int y_stride, uint16_t* y_dump, hipStream_t stream) {
   GemmArgs a{};
   a.eoff = eoff; a.E = E; a.split = 1; a.mx = 1;
   a.act = aq; a.act_scale = (const float*)ae; a.w = w2; a.w_scale = (const float*)w2e;
   a.sorted_ids = sorted_ids; a.expert_ids = expert_ids; a.ntpp = ntpp;
   a.y_out = y; a.y_stride = y_stride;
-  a.y_rows = nblk * BM; a.y_cols = y_stride; a.y_dump = y; a.ksplit = 1;
+  a.y_rows = nblk * BM; a.y_cols = y_stride; a.y_dump = y_dump; a.ksplit = 1;
   a.K = I; a.N = H; a.I = I; a.H = H; a.P = P; a.top_k = 1;
   a.n_tiles = (H + 255) / 256; a.nblk = nblk;
   return launch_gemm2_bm(a, BM, stream);

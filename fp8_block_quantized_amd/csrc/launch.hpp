@@ -44,7 +44,7 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
 hipError_t launch_gemm2(const uint8_t* aq, const float* as, const uint8_t* w2, const float* w2s,
                         const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                         const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
-                        uint16_t* y, int y_stride, int kslices, float* y_slices,
+                        uint16_t* y, int y_stride, uint16_t* y_dump, int kslices, float* y_slices,
                         hipStream_t stream);
 // The MXFP8 layer's GEMMs (block_m 16 to 128): exponent bytes [rows, K/32]
 // for the activations, [E, N, K/32] for the weights; GEMM1 writes the
@@ -56,7 +56,7 @@ hipError_t launch_gemm1_mx(const uint8_t* xq, const uint8_t* xe, const uint8_t* 
 hipError_t launch_gemm2_mx(const uint8_t* aq, const uint8_t* ae, const uint8_t* w2, const uint8_t* w2e,
                            const int32_t* sorted_ids, const int32_t* expert_ids, const int32_t* ntpp,
                            const int32_t* eoff, int E, int H, int I, int P, int BM, int nblk,
-                           uint16_t* y, int y_stride, hipStream_t stream);
+                           uint16_t* y, int y_stride, uint16_t* y_dump, hipStream_t stream);
 // GEMM2 with an output bounded to rows [0, y_rows) and columns [0, y_cols):
 // stores outside go to a 1024-byte dump; with ksplit > 1, K slices go to
 // float32 partials [ksplit, y_rows, y_cols] and are summed into y (the dense linear).

@@ -12,6 +12,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr size_t kDumpBytes = 1024;   // after y: the second GEMM's stores of padding row groups
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // row stride of the per-pair outputs: whole 256-feature tiles, so that the
@@ -113,7 +114,7 @@ void make_layout(int T, int H, int I, int E, int top_k, Layout& L, int block_m =
   sz[MOE_TAP_XS] = (size_t)T * (H / 128) * 4;
   sz[MOE_TAP_AQ] = L.cap * I;
   sz[MOE_TAP_AS] = L.cap * (I / 128) * 4;
-  sz[MOE_TAP_Y] = L.cap * y_stride(H) * 2;
+  sz[MOE_TAP_Y] = L.cap * y_stride(H) * 2 + kDumpBytes;
   sz[MOE_TAP_ALIGN_SCRATCH] = moe::align_scratch_bytes((int)P, E);
   sz[MOE_TAP_Y_SLICES] = L.kslices > 1 ? (size_t)L.kslices * P * y_stride(H) * 4 : 0;
   sz[MOE_TAP_H_SLICES] = L.kslices1 > 1 ? (size_t)L.kslices1 * P * 2 * I * 8 : 0;
@@ -348,8 +349,9 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
     return MOE_ERR_HIP;
   if (mark(4)) return MOE_ERR_HIP;
   float* yslices = (float*)(ws + L.off[MOE_TAP_Y_SLICES]);
+  uint16_t* ydump = y + L.cap * y_stride(H);
   if ((err = moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, EL, H, I, P, L.BM,
-                               nblk, y, (int)y_stride(H), L.kslices, yslices, stream)))
+                               nblk, y, (int)y_stride(H), ydump, L.kslices, yslices, stream)))
     return MOE_ERR_HIP;
   if (mark(5)) return MOE_ERR_HIP;
   if (L.kslices > 1)
@@ -458,7 +460,7 @@ int moe_fp8_batched_experts(const void* x, const int32_t* expert_num_tokens, con
                         nblk, aq, as, 1, nullptr, nullptr, stream))
     return MOE_ERR_HIP;
   if (moe::launch_gemm2(aq, as, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, T, L.BM, nblk, y,
-                        (int)y_stride(H), 1, nullptr, stream))
+                        (int)y_stride(H), y + L.cap * y_stride(H), 1, nullptr, stream))
     return MOE_ERR_HIP;
   if (moe::launch_combine(y, (int)y_stride(H), ppos, nullptr, T, H, 1, (uint16_t*)out, stream))
     return MOE_ERR_HIP;
@@ -534,7 +536,7 @@ int moe_fp8_mx_forward(const void* x, const float* router_logits, const uint8_t*
                            L.BM, nblk, aq, ae, stream))
     return MOE_ERR_HIP;
   if (moe::launch_gemm2_mx(aq, ae, w2, w2_scale, sorted, eids, ntpp, eoff, E, H, I, P, L.BM, nblk, y,
-                           (int)y_stride(H), stream))
+                           (int)y_stride(H), y + L.cap * y_stride(H), stream))
     return MOE_ERR_HIP;
   if (moe::launch_combine(y, (int)y_stride(H), ppos, tw, T, H, top_k, (uint16_t*)out, stream))
     return MOE_ERR_HIP;
