@@ -11,7 +11,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_fp8.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_fp8.cpp", "quant.hip", "router.hip", "align.hip", "gemm.hip", "combine.hip",
+SOURCES = ["moe_fp8.cpp", "quant.hip", "router.hip", "align.hip", "front.hip", "gemm.hip", "combine.hip",
            "probe.hip"]
 
 # -ffp-contract=off: the arithmetic is exactly as written (explicit fmaf where

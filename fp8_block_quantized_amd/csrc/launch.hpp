@@ -25,6 +25,17 @@ const int32_t* align_expert_offsets(const void* scratch, int P, int E);
 hipError_t launch_align(const int32_t* ids, const int32_t* emap, int n_map, int P, int E, int BM,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp, int32_t* pair_pos,
                         void* scratch, hipStream_t stream);
+// The router, the single-workgroup sort-and-pad and the group-128 quant of a
+// decode batch in one launch (decode_front_fits: T <= 16, T * top_k <= 1024,
+// E <= 512), with the same outputs as launch_topk_softmax + launch_align +
+// launch_group_quant.
+bool decode_front_fits(int T, int E, int top_k);
+hipError_t launch_decode_front(const float* logits, int T, int E, int top_k, int renormalize,
+                               int num_group, int topk_group, const int32_t* emap, int n_map,
+                               int EL, int BM, const void* x, int H, int32_t* ids, float* tw,
+                               int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
+                               int32_t* eoff, int32_t* pair_pos, uint8_t* xq, float* xs,
+                               hipStream_t stream);
 hipError_t launch_identity_layout(int M, int BM, int nblk, int32_t* sorted_ids,
                                   int32_t* expert_ids, int32_t* eoff, int32_t* ntpp,
                                   hipStream_t stream);

@@ -332,16 +332,26 @@ static int forward_impl(const void* x, const float* router_logits, const uint8_t
   hipError_t err;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if (mark(0)) return MOE_ERR_HIP;
-  if ((err = moe::launch_topk_softmax(router_logits, T, E, top_k, renormalize, route.num_group,
-                                      route.topk_group, ids, tw, stream)))
-    return MOE_ERR_HIP;
-  if (mark(1)) return MOE_ERR_HIP;
-  if ((err = moe::launch_align(ids, route.emap, E, P, EL, L.BM, sorted, eids, ntpp, ppos, scratch,
-                               stream)))
-    return MOE_ERR_HIP;
-  if (mark(2)) return MOE_ERR_HIP;
-  if ((err = moe::launch_group_quant(x, T, H, xq, xs, stream))) return MOE_ERR_HIP;
-  if (mark(3)) return MOE_ERR_HIP;
+  if (moe::decode_front_fits(T, E, top_k)) {
+    // one launch for the three front stages (their events all mark its end)
+    int32_t* eoffw = (int32_t*)moe::align_expert_offsets(scratch, P, EL);
+    if ((err = moe::launch_decode_front(router_logits, T, E, top_k, renormalize, route.num_group,
+                                        route.topk_group, route.emap, E, EL, L.BM, x, H, ids, tw,
+                                        sorted, eids, ntpp, eoffw, ppos, xq, xs, stream)))
+      return MOE_ERR_HIP;
+    if (mark(1) || mark(2) || mark(3)) return MOE_ERR_HIP;
+  } else {
+    if ((err = moe::launch_topk_softmax(router_logits, T, E, top_k, renormalize, route.num_group,
+                                        route.topk_group, ids, tw, stream)))
+      return MOE_ERR_HIP;
+    if (mark(1)) return MOE_ERR_HIP;
+    if ((err = moe::launch_align(ids, route.emap, E, P, EL, L.BM, sorted, eids, ntpp, ppos, scratch,
+                                 stream)))
+      return MOE_ERR_HIP;
+    if (mark(2)) return MOE_ERR_HIP;
+    if ((err = moe::launch_group_quant(x, T, H, xq, xs, stream))) return MOE_ERR_HIP;
+    if (mark(3)) return MOE_ERR_HIP;
+  }
   const int32_t* eoff = moe::align_expert_offsets(scratch, P, EL);
   double* hslices = (double*)(ws + L.off[MOE_TAP_H_SLICES]);
   if ((err = moe::launch_gemm1(xq, xs, w13, w13_scale, sorted, eids, ntpp, eoff, EL, H, I, P,

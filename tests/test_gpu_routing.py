@@ -89,6 +89,11 @@ def _routed_case(T, H, I, E, k, G, kg, local, seed, what):
     (400, 256, 256, 8, 2, 1, 1, [1, 2, 6]),            # expert map, 128-row blocks
     (64, 512, 256, 64, 6, 8, 3, list(range(16, 32))),  # both, one linear rank of four
     (256, 256, 128, 32, 4, 4, 2, list(range(1, 32, 4))),  # both, round-robin placement
+    # at most 16 tokens: the one-launch front end (routing, layout, quant)
+    (1, 256, 256, 16, 4, 4, 2, None),                  # grouped, one token
+    (16, 256, 384, 12, 3, 1, 1, [0, 5, 7, 11]),        # expert map, sixteen tokens
+    (5, 512, 256, 64, 6, 8, 3, list(range(16, 32))),   # both
+    (16, 256, 256, 512, 8, 1, 1, None),                # 512 experts
 ])
 def test_routed_forward(T, H, I, E, k, G, kg, local):
     _routed_case(T, H, I, E, k, G, kg, local, seed=T + H + I + E + k + G, what="routed")
