@@ -61,12 +61,12 @@ TARGETS = {("tiny", 16): None, ("mixtral", 64): ("hbm", 0.6), ("mixtral", 512): 
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
 # kernel source they were taken on: the line reports null traffic once
 # gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "c57127a888b3849badba0b4dbc0ef443f82969b6c542f60ea5be158607bd4216"
+TRAFFIC_SOURCE_SHA256 = "f02ceff886285dd4a898c7148d711f29f56c09e32a5c0cdc89b207d14cf1ebd7"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
-    "prefill.gemm1": (10748266557, 184470912),
-    "prefill.gemm2": (4397065067, 1208267115),
-    "decode.gemm1": (4795674564, 5724203),
-    "decode.gemm2": (2408673012, 7340288),
+    "prefill.gemm1": (10762680997, 184494421),
+    "prefill.gemm2": (4839649405, 968238325),
+    "decode.gemm1": (4795704131, 5723755),
+    "decode.gemm2": (2408918724, 7340299),
 }
 
 
@@ -510,7 +510,13 @@ def run_peaks(args, moe, dev):
     return peaks
 
 
+def progress(what, t0):
+    """one line per finished section on stderr, so a long run shows it is alive"""
+    print(f"[bench] {what} done after {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+
 def main():
+    t_start = time.perf_counter()
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -563,6 +569,7 @@ def main():
         out["ms_per_step"] = layer["wall_s"] / args.steps * 1e3
         out["step_ms"] = layer["step_ms"]
         out["phases"] = layer["phases"]
+        progress("layer", t_start)
 
     if args.copy_calibration_mib:
         nb = args.copy_calibration_mib << 20
@@ -577,15 +584,23 @@ def main():
     if "configs" in args.sections:
         out["configs"] = run_configs(args, moe, dev, skip={(args.workload, T) for T in (T_dec, T_pre)}
                                      if layer else set())
+        progress("configs", t_start)
     if "quant" in args.sections:
         out["quant_standalone"] = run_quant(args, moe, dev)
+        progress("quant", t_start)
     if "linear" in args.sections:
         out["dense_linear"], out["dense_linear_mxfp8"] = run_linear(args, moe, dev)
+        progress("linear", t_start)
     if "batched" in args.sections:
         out["batched_experts"] = run_batched(args, moe, dev)
+        progress("batched", t_start)
     if "mx" in args.sections:
         out["moe_mxfp8"] = run_mx(args, moe, dev, c, phases, order)
-    peaks = run_peaks(args, moe, dev) if "peaks" in args.sections else None
+        progress("mx", t_start)
+    peaks = None
+    if "peaks" in args.sections:
+        peaks = run_peaks(args, moe, dev)
+        progress("peaks", t_start)
     out["measured_peaks"] = peaks
     out["roofline"] = dominant_roofline(layer["kernels"], args.workload, peaks) if layer else None
     out["kernels"] = layer["kernels"] if layer else None
