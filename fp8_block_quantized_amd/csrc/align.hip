@@ -43,6 +43,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
     int32_t* __restrict__ base, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp, int32_t* __restrict__ eoff) {
   __shared__ int scan[kChunk];
+  __shared__ int wsum[kChunk / 64];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
@@ -50,15 +51,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
     for (int b = 0; b < nchunk; ++b) total += counts[(size_t)b * E + e];
   }
   const int pad = (total + BM - 1) / BM * BM;
-  scan[e] = pad;
-  __syncthreads();
-  for (int off = 1; off < kChunk; off <<= 1) {
-    const int v = e >= off ? scan[e - off] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
-  const int incl = scan[e];
+  const int incl = block_inclusive_scan(pad, scan, wsum);
   const int excl = incl - pad;
   const int padded_total = scan[kChunk - 1];
   if (e == 0) ntpp[0] = padded_total;
@@ -168,6 +161,7 @@ __global__ __launch_bounds__(1024) void batched_layout_kernel(
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp, int32_t* __restrict__ eoff,
     int32_t* __restrict__ pair_pos) {
   __shared__ int scan[kChunk];
+  __shared__ int wsum[kChunk / 64];
   __shared__ int cnt[kMaxE], off[kMaxE];
   const int e = threadIdx.x;
   int c = 0;
@@ -177,14 +171,7 @@ __global__ __launch_bounds__(1024) void batched_layout_kernel(
     cnt[e] = c;
   }
   const int pad = (c + BM - 1) / BM * BM;
-  scan[e] = pad;
-  __syncthreads();
-  for (int o = 1; o < kChunk; o <<= 1) {
-    const int v = e >= o ? scan[e - o] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
+  block_inclusive_scan(pad, scan, wsum);
   const int total = scan[kChunk - 1];
   if (e < E) {
     off[e] = scan[e] - pad;

@@ -23,7 +23,36 @@ struct AlignSingleLds {
   int hist[kMaxE];
   int scan[kChunk];
   int wcnt[kChunk / 64][kMaxE];
+  int wsum[kChunk / 64];
 };
+
+// Inclusive prefix sum of v over the kChunk threads of the workgroup, also
+// stored to scan[t]: a shuffle scan inside each wave, the 16 wave totals
+// scanned by wave 0, then each wave's offset added (three barriers).
+__device__ __forceinline__ int block_inclusive_scan(int v, int* scan, int* wsum) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kChunk / 64 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kChunk / 64; off <<= 1) {
+      const int o = __shfl_up(w, off);
+      if (lane >= off) w += o;
+    }
+    if (lane < kChunk / 64) wsum[lane] = w;
+  }
+  __syncthreads();
+  if (wave > 0) v += wsum[wave - 1];
+  scan[t] = v;
+  __syncthreads();
+  return v;
+}
 
 // Count, scan and scatter of P <= kChunk pairs by one workgroup of kChunk
 // threads: the histogram, the padded offsets and the ranks stay in LDS, and
@@ -49,15 +78,7 @@ __device__ __forceinline__ void align_single(AlignSingleLds& s, const int32_t* i
   // 2. padded offsets, sentinels, block -> expert table
   const int total = t < E ? s.hist[t] : 0;
   const int pad = (total + BM - 1) / BM * BM;
-  s.scan[t] = pad;
-  __syncthreads();
-  for (int off = 1; off < kChunk; off <<= 1) {
-    const int v = t >= off ? s.scan[t - off] : 0;
-    __syncthreads();
-    s.scan[t] += v;
-    __syncthreads();
-  }
-  const int excl = s.scan[t] - pad;
+  const int excl = block_inclusive_scan(pad, s.scan, s.wsum) - pad;
   const int padded_total = s.scan[kChunk - 1];
   if (t == 0) {
     ntpp[0] = padded_total;

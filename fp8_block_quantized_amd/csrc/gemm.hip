@@ -555,6 +555,8 @@ __global__ __launch_bounds__(256) void moe_gemm1_kernel(GemmArgs args, int BM, i
   }
 }
 
+constexpr int kMaxGemm1Slices = 8;
+
 // The end of moe_gemm1_kernel<RM, true>: per pair p (at sorted row pair_pos[p])
 // and 128-feature group j, h = the float64 sum of the slices' partials in
 // slice order, then a = float32(silu(gate) * up) evaluated in float64, the
@@ -575,13 +577,26 @@ __global__ __launch_bounds__(256) void gemm1_slices_finish_kernel(const double* 
   float a[4] = {0.f, 0.f, 0.f, 0.f};
   float m = 0.0f;
   if (row >= 0) {
+    // every slice's loads in flight together (kslices <= kMaxGemm1Slices), then
+    // the sums in slice order
+    double2 g0[kMaxGemm1Slices], g1[kMaxGemm1Slices], u0[kMaxGemm1Slices], u1[kMaxGemm1Slices];
+#pragma unroll
+    for (int s = 0; s < kMaxGemm1Slices; ++s) {
+      if (s < kslices) {
+        const double* h = hs + ((size_t)s * P + p) * (2 * (size_t)I);
+        g0[s] = *(const double2*)(h + i);
+        g1[s] = *(const double2*)(h + i + 2);
+        u0[s] = *(const double2*)(h + I + i);
+        u1[s] = *(const double2*)(h + I + i + 2);
+      }
+    }
     double gt[4] = {0.0, 0.0, 0.0, 0.0}, up[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int s = 0; s < kslices; ++s) {
-      const double* h = hs + ((size_t)s * P + p) * (2 * (size_t)I);
-      const double2 g0 = *(const double2*)(h + i), g1 = *(const double2*)(h + i + 2);
-      const double2 u0 = *(const double2*)(h + I + i), u1 = *(const double2*)(h + I + i + 2);
-      gt[0] += g0.x; gt[1] += g0.y; gt[2] += g1.x; gt[3] += g1.y;
-      up[0] += u0.x; up[1] += u0.y; up[2] += u1.x; up[3] += u1.y;
+#pragma unroll
+    for (int s = 0; s < kMaxGemm1Slices; ++s) {
+      if (s < kslices) {
+        gt[0] += g0[s].x; gt[1] += g0[s].y; gt[2] += g1[s].x; gt[3] += g1[s].y;
+        up[0] += u0[s].x; up[1] += u0[s].y; up[2] += u1[s].x; up[3] += u1[s].y;
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1660,7 +1675,8 @@ hipError_t launch_gemm1(const uint8_t* xq, const float* xs, const uint8_t* w13, 
                         const int32_t* eoff, int E, int H, int I, int P, int top_k, int BM, int nblk,
                         uint8_t* aq, float* as, int kslices, double* h_slices,
                         const int32_t* pair_pos, hipStream_t stream) {
-  if (kslices > 1 && (BM > 64 || !h_slices || !pair_pos || kslices > (H >> 7)))
+  if (kslices > 1 && (BM > 64 || !h_slices || !pair_pos || kslices > (H >> 7) ||
+                      kslices > kMaxGemm1Slices))
     return hipErrorInvalidValue;
   GemmArgs a{};
   a.eoff = eoff; a.E = E;
