@@ -61,12 +61,12 @@ TARGETS = {("tiny", 16): None, ("mixtral", 64): ("hbm", 0.6), ("mixtral", 512): 
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
 # kernel source they were taken on: the line reports null traffic once
 # gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "f02ceff886285dd4a898c7148d711f29f56c09e32a5c0cdc89b207d14cf1ebd7"
+TRAFFIC_SOURCE_SHA256 = "912f0ae2a5353abf7d1e0e292333ab8d01cf6a12286cf5b18ee0b918d0f174de"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
-    "prefill.gemm1": (10762680997, 184494421),
-    "prefill.gemm2": (4839649405, 968238325),
-    "decode.gemm1": (4795704131, 5723755),
-    "decode.gemm2": (2408918724, 7340299),
+    "prefill.gemm1": (10763120674, 184532992),
+    "prefill.gemm2": (4857224361, 968246581),
+    "decode.gemm1": (4795608859, 5723072),
+    "decode.gemm2": (2408905797, 7340299),
 }
 
 
@@ -203,11 +203,11 @@ def cpu_baseline(w, x_dec, logits_dec, k, n_tok):
 
 
 def timed_calls(fn, n, warmup=3):
-    """fn() n times after warmup, each call bracketed by HIP events on the
-    current stream; returns the per-call milliseconds."""
+    """fn(i) for i < n after fn(0 .. warmup - 1), each timed call bracketed by
+    HIP events on the current stream; returns the per-call milliseconds."""
     import torch
-    for _ in range(warmup):
-        fn(0)
+    for i in range(warmup):
+        fn(i)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     torch.cuda.synchronize()
@@ -340,8 +340,12 @@ def run_configs(args, moe, dev, skip):
             x, logits = make_activations(H, E, T, base, c["logits"], dev)
             ws = moe.alloc_workspace(T, H, I, E, k, dev)
             o = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            # the warm-up calls go once round the replicas, so that the timed
+            # calls see the steady state of the rotation (no first touch of a
+            # replica's pages inside the timed region)
             ms = timed_calls(lambda i: moe.moe_fp8_forward(x, logits, *reps[i % nrep], k, True,
-                                                           out=o, workspace=ws), args.steps)
+                                                           out=o, workspace=ws), args.steps,
+                             warmup=max(3, nrep))
             taps = moe.workspace_taps(ws, T, H, I, E, k)
             alg = algorithmic(taps["topk_ids"].cpu().numpy(), T, H, I, E, k)
             sm = stats(ms)
