@@ -204,13 +204,20 @@ def cpu_baseline(w, x_dec, logits_dec, k, n_tok):
 
 def timed_calls(fn, n, warmup=3):
     """fn(i) for i < n after fn(0 .. warmup - 1), each timed call bracketed by
-    HIP events on the current stream; returns the per-call milliseconds."""
+    HIP events on the current stream; returns the per-call milliseconds.
+
+    The timed calls are enqueued right behind the warm-up calls, with no
+    synchronisation in between, so the GPU never waits on the host between
+    two launches: each pair of events measures the call's GPU time, as a
+    back-to-back or graph-replayed loop sees it.  (After an idle GPU the
+    first calls of a microsecond-scale layer would also measure the host's
+    launch latency.)"""
     import torch
-    for i in range(warmup):
-        fn(i)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     torch.cuda.synchronize()
+    for i in range(warmup):
+        fn(i)
     for i in range(n):
         ev[i][0].record()
         fn(i)
