@@ -12,8 +12,9 @@ and activation codes bit for bit, routing weights within 1e-5, requantised
 codes through the tie window, the output within the bar).  The dense
 block-FP8 linear (12 shapes, every output), grouped top-k with random
 expert maps (8 shapes, the checks of test_gpu_routing.py) and the batched
-format with random counts (8 shapes, the checks of test_gpu_batched.py)
-likewise."""
+format with random counts (8 shapes, the checks of test_gpu_batched.py),
+the MXFP8 layer (8 shapes, the checks of test_gpu_mx_forward.py) and the
+MXFP8 linear (8 shapes, every output) likewise."""
 
 import numpy as np
 import pytest
@@ -21,11 +22,17 @@ import torch
 
 import fp8_block_quantized_amd as moe
 from oracle import linear as ref_linear
-from synth import make_linear, make_weights
+from oracle import moe as ref_moe
+from synth import make_activations, make_linear, make_mx_linear, make_mx_weights, make_weights
 from tests.gpu_util import assert_out_close, note, np_
 from tests.test_gpu_batched import _check as _batched_check
 from tests.test_gpu_batched import _inputs as _batched_inputs
 from tests.test_gpu_forward import _full_case, _layer
+from tests.test_gpu_linear import _mx_check as _mx_linear_check
+from tests.test_gpu_mx_forward import _check_front as _mx_check_front
+from tests.test_gpu_mx_forward import _compare_mx_requant
+from tests.test_gpu_mx_forward import _requant_of_pairs as _mx_requant_of_pairs
+from tests.test_gpu_mx_forward import _run as _mx_run
 from tests.test_gpu_routing import _routed_case
 
 pytestmark = pytest.mark.gpu
@@ -119,3 +126,47 @@ def test_random_batched(i, E, M, H, I, counts):
                                       *[a.cuda() for a in w], workspace=wsp)
     torch.cuda.synchronize()
     _batched_check(x, counts, w, out, wsp, E, M, H, I, f"random batched #{i}")
+
+
+def _mx_layer_shapes(n=8, seed=1717):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 5, 17, 64, 130, 300]))
+        H = 128 * int(rng.integers(1, 7))
+        I = 128 * int(rng.integers(2, 7))        # the MXFP8 layer needs I >= 256
+        out.append((i, T, H, I, E, k))
+    return out
+
+
+@pytest.mark.parametrize("i,T,H,I,E,k", _mx_layer_shapes())
+def test_random_mx_layer(i, T, H, I, E, k):
+    """the MXFP8 layer on seeded random shapes, with test_gpu_mx_forward.py's checks"""
+    note(f"random mx layer #{i} T={T} H={H} I={I} E={E} k={k}")
+    w13, w13e, w2, w2e = make_mx_weights(H, I, E, 8000 + 7 * i)
+    x, logits = make_activations(H, E, T, 8100 + 7 * i)
+    out, taps = _mx_run(x.cuda(), logits.cuda(), [a.cuda() for a in (w13, w13e, w2, w2e)],
+                        T, H, I, E, k)
+    ref, info = ref_moe.moe_forward(x.float().numpy(), logits.numpy(), w13.numpy(), w13e.numpy(),
+                                    w2.numpy(), w2e.numpy(), k, True, mx=True)
+    rows = _mx_check_front(taps, x.float().numpy(), info["ids"], info["w"], E)
+    g, ge = _mx_requant_of_pairs(taps, rows, np.arange(T * k), T * k)
+    mm, n = _compare_mx_requant(g, ge, info["aq"], info["as"])
+    assert mm * n <= 0.01 * n + 3, f"requant mismatch fraction {mm}"
+    assert_out_close(np_(out.float()), ref, f"random mx layer #{i}")
+
+
+def _mx_linear_shapes(n=8, seed=2929):
+    rng = np.random.default_rng(seed)
+    return [(i, int(rng.integers(1, 700)), 128 * int(rng.integers(1, 13)), 128 * int(rng.integers(2, 13)))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("i,M,N,K", _mx_linear_shapes())
+def test_random_mx_linear(i, M, N, K):
+    """the MXFP8 linear on seeded random shapes (K >= 256), every output"""
+    x, w, we = make_mx_linear(M, N, K, seed_base=9500 + 11 * i)
+    note(f"random mx linear #{i} M={M} N={N} K={K}")
+    _mx_linear_check(x, w, we, f"random mx linear #{i} {M}x{N}x{K}")
