@@ -110,6 +110,12 @@ __device__ __forceinline__ void barrier_raw() { asm volatile("s_barrier" ::: "me
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// a compile-time int for generic lambdas (loops instantiated per count)
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 template <typename T>
 __device__ __forceinline__ T load_uniform(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
@@ -907,10 +913,13 @@ __global__ __launch_bounds__(512) void moe_gemm2_pf_kernel(GemmArgs args) {
 // relative error of a few 1e-7, far below one e4m3 step of a.  Operands stay
 // e4m3 in a three-stage LDS ring filled by direct global->LDS loads (XOR
 // swizzle on 16-byte chunks, no bank conflicts on the 16-byte reads).
-// Padding rows sit at the end of an expert's last block, so a wave whose 64
-// token rows start with the sentinel has no real row: it still loads its
-// share of every stage and meets every barrier, but skips its conversions,
-// MFMAs and folds (its rows' outputs are never read).
+// Padding rows sit at the end of an expert's last block, so the real rows of
+// a wave's 64 form a prefix of its four 16-row groups.  The K loop is
+// instantiated for 0-4 live groups: every wave loads its share of every
+// stage and meets every barrier, but converts, multiplies and folds only the
+// token fragments of its live groups (the other rows' outputs are never
+// read); in the last block of an expert that drops the MFMAs of up to 48
+// padding rows per wave.
 constexpr int kPf1Stages = 3;
 constexpr int kPf1W = 256 * 128, kPf1A = 128 * 128, kPf1S = 2048;
 constexpr int kPf1Stage = kPf1W + kPf1A + kPf1S;
@@ -930,7 +939,10 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
   const int e = load_uniform(args.expert_ids + b);
   const int K = args.K, nkb = K >> 7, I = args.I, i0 = 128 * j;
   const int row0 = b * BM;
-  const bool live = load_uniform(args.sorted_ids + row0 + 64 * wt) < args.P;
+  // live 16-row groups of this wave's rows: those whose first row is real
+  int nlive = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) nlive += load_uniform(args.sorted_ids + row0 + 64 * wt + 16 * q) < args.P;
 
   // this lane's share of a stage: 4 x 16 bytes of weights, 2 x 16 of tokens
   const uint8_t* wsrc[4];
@@ -996,41 +1008,53 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
     return *(const v8h*)h;
   };
 
-  issue(0, 0);
-  if (nkb > 1) issue(1, 1);
-  for (int kb = 0; kb < nkb; ++kb) {
-    // stage kb has landed once at most the next stage's loads are pending
-    if (kb + 1 < nkb) wait_vmem<kPf1Loads>(); else wait_vmem<0>();
-    barrier_raw();
-    if (kb + 2 < nkb) issue((kb + 2) % kPf1Stages, kb + 2);
-    if (!live) continue;
-    const uint8_t* st = ring + (kb % kPf1Stages) * kPf1Stage;
-    const float swg = load_uniform(wsg + kb), swu = load_uniform(wsu + kb);
-    float sa[4];
+  // the K loop with NQ live token groups (the same loads, waits and barriers
+  // for every NQ)
+  auto kloop = [&](auto nq_c) {
+    constexpr int NQ = decltype(nq_c)::value, NA = NQ > 0 ? NQ : 1;
+    issue(0, 0);
+    if (nkb > 1) issue(1, 1);
+    for (int kb = 0; kb < nkb; ++kb) {
+      // stage kb has landed once at most the next stage's loads are pending
+      if (kb + 1 < nkb) wait_vmem<kPf1Loads>(); else wait_vmem<0>();
+      barrier_raw();
+      if (kb + 2 < nkb) issue((kb + 2) % kPf1Stages, kb + 2);
+      if (NQ == 0) continue;
+      const uint8_t* st = ring + (kb % kPf1Stages) * kPf1Stage;
+      const float swg = load_uniform(wsg + kb), swu = load_uniform(wsu + kb);
+      float sa[NA];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sa[q] = *(const float*)(st + kPf1W + kPf1A + (64 * wt + 16 * q + l16) * 4);
-    v4f part[4][4];
+      for (int q = 0; q < NQ; ++q) sa[q] = *(const float*)(st + kPf1W + kPf1A + (64 * wt + 16 * q + l16) * 4);
+      v4f part[4][NA];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v8h wf[4], tf[4];
+      for (int c = 0; c < 4; ++c) {
+        v8h wf[4], tf[NA];
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) wf[pp] = frag(st + pw[pp][c >> 1] + 8 * (c & 1));
+        for (int pp = 0; pp < 4; ++pp) wf[pp] = frag(st + pw[pp][c >> 1] + 8 * (c & 1));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tf[q] = frag(st + pa[q][c >> 1] + 8 * (c & 1));
+        for (int q = 0; q < NQ; ++q) tf[q] = frag(st + pa[q][c >> 1] + 8 * (c & 1));
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
+        for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          part[pp][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp], tf[q], c == 0 ? zero : part[pp][q], 0, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const float sc = sa[q] * (pp < 2 ? swg : swu);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[pp][q][r], sc, acc[pp][q][r]);
+          for (int q = 0; q < NQ; ++q)
+            part[pp][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[pp], tf[q], c == 0 ? zero : part[pp][q], 0, 0, 0);
       }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const float sc = sa[q] * (pp < 2 ? swg : swu);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[pp][q][r] = __builtin_fmaf(part[pp][q][r], sc, acc[pp][q][r]);
+        }
+    }
+  };
+  switch (nlive) {
+    case 0: kloop(IntC<0>{}); break;
+    case 1: kloop(IntC<1>{}); break;
+    case 2: kloop(IntC<2>{}); break;
+    case 3: kloop(IntC<3>{}); break;
+    default: kloop(IntC<4>{}); break;
   }
 
   // a = silu(gate) * up in float32, then the per-row requant over the 128
