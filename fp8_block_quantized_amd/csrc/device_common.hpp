@@ -76,6 +76,40 @@ __device__ __forceinline__ float wave_max_xor(float v, int first_mask, int last_
   return v;
 }
 
+// Lane exchanges inside rows of 16 lanes by DPP (register reads, no LDS
+// round trip as a shuffle takes): the gfx9 data-parallel-primitive controls
+// for lane ^ 1 and lane ^ 2 (quad permutations), and the mirrors of each
+// half row (lane i <-> 7 - i) and of each row (lane i <-> 15 - i).  After the
+// two quad steps a quad holds one value, so the half-row mirror then pairs
+// whole quads and the row mirror whole half rows: the four steps reduce a
+// row as a butterfly over 16 lanes would.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_float(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Maximum over aligned groups of LPG lanes (2, 4, 8 or 16), in every lane
+// of the group; max is exact, so the order of the steps does not matter.
+template <int LPG>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(LPG == 2 || LPG == 4 || LPG == 8 || LPG == 16, "lanes per group");
+  v = __builtin_fmaxf(v, dpp_float<kDppXor1>(v));
+  if (LPG >= 4) v = __builtin_fmaxf(v, dpp_float<kDppXor2>(v));
+  if (LPG >= 8) v = __builtin_fmaxf(v, dpp_float<kDppHalfMirror>(v));
+  if (LPG >= 16) v = __builtin_fmaxf(v, dpp_float<kDppMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float read_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 // Hardware dispatches consecutive workgroup ids round-robin over the eight
 // XCDs.  Renumber them so that each XCD receives a contiguous range of
 // logical ids: tiles that share a weight panel then run on one XCD and meet

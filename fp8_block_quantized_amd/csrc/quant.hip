@@ -15,7 +15,8 @@
 // sequence of M*K/G groups of G bf16 values.  G/8 lanes own one group, each
 // lane 8 consecutive values (one 16-byte load), so a wave covers 1 KiB of
 // contiguous input per step and every access is a full, aligned vector load
-// or store.  The group amax is a butterfly over its lanes; the scale and its
+// or store.  The group amax is a DPP reduction over its lanes (quad swaps,
+// then the half-row and row mirrors); the scale and its
 // reciprocal are computed once per lane, and every element costs one
 // multiply and two FMAs for the correctly rounded quotient (one multiply for
 // a power-of-two scale).  HBM bound: 2 bytes in, 1 byte + 4/G (or 1/G)

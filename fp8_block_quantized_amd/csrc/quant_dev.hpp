@@ -33,7 +33,7 @@ __device__ __forceinline__ void quant_slots(const uint4* __restrict__ x, uint2* 
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
-    amax = wave_max_xor(amax, LPG / 2, 1);   // the lanes of this group
+    amax = group_max<LPG>(amax);             // the lanes of this group
     float s, r;
     group_scale(amax, s, r);
     float d[8];

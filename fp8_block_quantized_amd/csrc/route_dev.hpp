@@ -9,17 +9,43 @@
 
 namespace moe {
 
-// Butterfly arg-max over the wave of (value, index), ties to the lower index;
-// lanes with index 0x7FFFFFFF hold no candidate.
-__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(bv, m);
-    const int oi = __shfl_xor(bi, m);
-    if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi))) {
-      bv = ov;
-      bi = oi;
-    }
+constexpr int kNoIndex = 0x7FFFFFFF;
+
+// (value, index) order of the selection: the larger value, ties to the
+// lower index; index kNoIndex holds no candidate.  A strict total order on
+// non-NaN values (-0 and +0 compare equal), so any reduction order picks
+// the same winner.
+__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
+  if (oi != kNoIndex && (bi == kNoIndex || ov > bv || (ov == bv && oi < bi))) {
+    bv = ov;
+    bi = oi;
   }
+}
+
+// Arg-max over the wave, the result in every lane: four DPP steps reduce
+// each row of 16 lanes, then the four row winners are read out in row order.
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  take_better(bv, bi, dpp_float<kDppXor1>(bv), dpp_int<kDppXor1>(bi));
+  take_better(bv, bi, dpp_float<kDppXor2>(bv), dpp_int<kDppXor2>(bi));
+  take_better(bv, bi, dpp_float<kDppHalfMirror>(bv), dpp_int<kDppHalfMirror>(bi));
+  take_better(bv, bi, dpp_float<kDppMirror>(bv), dpp_int<kDppMirror>(bi));
+  float v = read_lane(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) take_better(v, i, read_lane(bv, r), __builtin_amdgcn_readlane(bi, r));
+  bv = v;
+  bi = i;
+}
+
+// Sum over the wave, the same bits in every lane: pairwise within each row
+// of 16 lanes (both lanes of a pair add the same two values), then the row
+// sums in row order.
+__device__ __forceinline__ float wave_sum(float z) {
+  z += dpp_float<kDppXor1>(z);
+  z += dpp_float<kDppXor2>(z);
+  z += dpp_float<kDppHalfMirror>(z);
+  z += dpp_float<kDppMirror>(z);
+  return ((read_lane(z, 0) + read_lane(z, 16)) + read_lane(z, 32)) + read_lane(z, 48);
 }
 
 // Token t of T (the calling wave's; t >= T: nothing is written).  srow: this
@@ -58,7 +84,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     bool taken = false;
     for (int r = 0; r < topk_group; ++r) {
       float bv = gm;
-      int bi = lane < num_group && !taken ? lane : 0x7FFFFFFF;
+      int bi = lane < num_group && !taken ? lane : kNoIndex;
       wave_argmax(bv, bi);
       keep |= 1ull << bi;
       if (lane == bi) taken = true;
@@ -73,15 +99,11 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
   float my_v = 0.0f, top_v = 0.0f;
   for (int j = 0; j < top_k; ++j) {
     float bv = 0.0f;
-    int bi = 0x7FFFFFFF;
+    int bi = kNoIndex;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int e = lane + 64 * i;
-      const bool ok = e < E && !((used >> i) & 1u);
-      if (ok && (bi == 0x7FFFFFFF || v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
+      if (e < E && !((used >> i) & 1u)) take_better(bv, bi, v[i], e);
     }
     wave_argmax(bv, bi);
     if (j == 0) top_v = bv;
@@ -90,16 +112,13 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
   }
   float denom;
   if (renormalize) {
-    float z = lane < top_k ? expf(my_v - top_v) : 0.0f;
-    for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m);
-    denom = z;
+    denom = wave_sum(lane < top_k ? expf(my_v - top_v) : 0.0f);
   } else {
     float z = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
       if (lane + 64 * i < E) z += expf(v[i] - top_v);
-    for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m);
-    denom = z;
+    denom = wave_sum(z);
   }
   if (lane < top_k) {
     ids[(size_t)t * top_k + lane] = my_id;

@@ -6,8 +6,9 @@
 // Selection compares the float32 logits themselves (softmax is monotone),
 // ties going to the lower expert index, so the chosen ids are an exact
 // integer result.  Each lane holds the logits of experts lane, lane+64, ...;
-// a selection round is a lane-local scan and a 6-step butterfly over
-// (value, index).  With renormalisation the full-softmax denominator cancels
+// a selection round is a lane-local scan and a wave arg-max over (value,
+// index): four DPP steps within each row of 16 lanes, then the four row
+// winners read out in order.  With renormalisation the full-softmax denominator cancels
 // and only the chosen logits enter the weights.
 //
 // Grouped variant (num_group > 1; the overview page's environment table
@@ -17,7 +18,7 @@
 // groups are kept (ties to the lower group), and the selection above runs on
 // the kept groups' experts only; the weights are unchanged (full softmax,
 // optional renormalisation).  The wave stages its logits in LDS, lanes below
-// num_group scan their group for its best logit, and topk_group butterfly
+// num_group scan their group for its best logit, and topk_group arg-max
 // rounds pick the groups.
 #include "device_common.hpp"
 #include "launch.hpp"
