@@ -61,12 +61,12 @@ TARGETS = {("tiny", 16): None, ("mixtral", 64): ("hbm", 0.6), ("mixtral", 512): 
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
 # kernel source they were taken on: the line reports null traffic once
 # gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "912f0ae2a5353abf7d1e0e292333ab8d01cf6a12286cf5b18ee0b918d0f174de"
+TRAFFIC_SOURCE_SHA256 = "59057a3b5dd3ba00bd6bdb257717b3fcdc70f54444a7b33f5e181c58e5e33c8b"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
-    "prefill.gemm1": (10763120674, 184532992),
-    "prefill.gemm2": (4857224361, 968246581),
-    "decode.gemm1": (4795608859, 5723072),
-    "decode.gemm2": (2408905797, 7340299),
+    "prefill.gemm1": (11285952866, 184021248),
+    "prefill.gemm2": (5035629129, 968259253),
+    "decode.gemm1": (4795568361, 5713685),
+    "decode.gemm2": (2408830357, 7340587),
 }
 
 
