@@ -6,10 +6,12 @@ targets in tests/test_gpu_stages.py); the product runs on FP8 MFMAs with a
 float32 accumulator, whose rounding reaches the bf16 output smoothly, so the
 output bar is the layer's: |gpu - ref| <= 1e-2 + 2e-2 |ref| everywhere and a
 relative norm error below 1e-2.  The small cases cover one and several
-128-row blocks, a ragged last block, an output width that is not a multiple
-of 256 (the stores past it go to the workspace's dump), K split into slices
-and not, two K blocks and a single one; a garbage-filled workspace must not
-change a bit of the output.  A 4096 x 4096 x 1024 case has 512 output tiles
+128-row blocks, ragged last blocks from 1 to 65 rows (the rows past M are
+the workspace's padding rows), an output width that is not a multiple of
+256 (the stores past it go to the workspace's dump), K split into slices
+(including counts of K blocks that do not divide evenly) and not, two K
+blocks and a single one; a garbage-filled workspace must not change a bit
+of the output, with many padding rows or few.  A 4096 x 4096 x 1024 case has 512 output tiles
 against one persistent workgroup per CU, so each workgroup runs two tiles
 back to back (the hand-counted waits between one tile's stores and the next
 tile's loads); it is compared on every output.  The MXFP8 cases add
@@ -32,10 +34,14 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (1, 128, 128),      # one row: 16-row blocks
-    (5, 256, 384),      # ragged 16-row block
-    (20, 384, 256),     # 32-row blocks
-    (40, 512, 256),     # 64-row blocks
+    (1, 128, 128),      # one row, one K block
+    (5, 256, 384),      # ragged block, three K blocks
+    (20, 384, 256),
+    (40, 512, 256),
+    (16, 256, 1024),    # eight K blocks split into slices
+    (33, 128, 2048),
+    (64, 384, 1152),    # nine K blocks split into three slices
+    (65, 256, 512),
     (100, 1024, 512),   # 128-row blocks, four K blocks
     (300, 640, 256),    # 128-row blocks, N not a multiple of 256, two K blocks
     (130, 256, 128),    # 128-row blocks with a single K block
@@ -64,6 +70,24 @@ def test_linear_workspace_contents_do_not_matter():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.isfinite(a.float()).all()
+
+
+def test_linear_small_m_workspace_contents_do_not_matter():
+    """A 128-row block that is almost all padding rows (read from the
+    workspace, never stored), with K split into slices."""
+    M, N, K = 5, 384, 1024
+    x, w, ws = make_linear(M, N, K, seed_base=79)
+    xd, wd, wsd = x.cuda(), w.cuda(), ws.cuda()
+    n = moe.fp8_block_linear_workspace_bytes(M, N, K)
+    clean = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    dirty = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    note("linear small-M workspace garbage")
+    a = moe.fp8_block_linear(xd, wd, wsd, workspace=clean)
+    b = moe.fp8_block_linear(xd, wd, wsd, workspace=dirty)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref, _ = ref_linear.block_fp8_linear(x.float().numpy(), w.numpy(), ws.numpy())
+    assert_out_close(np_(a.float()), ref, "linear small-M garbage workspace")
 
 
 def _rows(M, seed):
@@ -131,6 +155,8 @@ def _mx_check(x, w, we, what, spread=False):
 @pytest.mark.parametrize("M,N,K", [
     (1, 128, 256),      # one row, K split in two slices
     (5, 256, 384),      # ragged block, three K blocks (no split)
+    (17, 128, 1024),
+    (64, 256, 1152),    # nine K blocks
     (100, 1024, 512),   # K split in two slices
     (300, 640, 256),    # N not a multiple of 256, two K blocks
     (130, 256, 2048),   # two row blocks, K split
@@ -146,8 +172,9 @@ def test_mx_linear_small(M, N, K, kind):
     _mx_check(x, w, we, f"mxfp8 linear {kind} {M}x{N}x{K}", spread=kind == "spread")
 
 
-def test_mx_linear_workspace_contents_do_not_matter():
-    M, N, K = 300, 640, 256
+@pytest.mark.parametrize("M", [5, 300])
+def test_mx_linear_workspace_contents_do_not_matter(M):
+    N, K = 640, 256
     x, w, we = make_mx_linear(M, N, K, seed_base=78)
     xd, wd, wed = x.cuda(), w.cuda(), we.cuda()
     n = moe.mxfp8_linear_workspace_bytes(M, N, K)
