@@ -59,15 +59,31 @@ TARGETS = {("tiny", 16): None, ("mixtral", 64): ("hbm", 0.6), ("mixtral", 512): 
 # HBM bytes per launch of the two GEMMs, from rocprofv3 FETCH_SIZE (x2) and
 # WRITE_SIZE (x1) passes, each scaled by what the same counter reads for a
 # plain 1 GiB copy (profiles/hbm_counters_dsv3_*.md).  Valid only for the
-# kernel source they were taken on: the line reports null traffic once
-# gemm.hip differs from this hash.
-TRAFFIC_SOURCE_SHA256 = "59057a3b5dd3ba00bd6bdb257717b3fcdc70f54444a7b33f5e181c58e5e33c8b"
+# kernel code they were taken on: the line reports null traffic once the code
+# of gemm.hip (kernel_code_digest: the file without its comments and blank
+# lines) differs from this digest.
+TRAFFIC_CODE_DIGEST = "f355efd5f8a833c1ec06e02486f4c97e5ed28a4025b35fd8c88a4556356b4231"
 TRAFFIC = {  # (read bytes, write bytes) per launch, DeepSeek-V3-shaped workload
     "prefill.gemm1": (11285952866, 184021248),
     "prefill.gemm2": (5035629129, 968259253),
     "decode.gemm1": (4795568361, 5713685),
     "decode.gemm2": (2408830357, 7340587),
 }
+
+
+def kernel_code_digest(path):
+    """sha256 of a C++ source without its // comments, trailing blanks and
+    blank lines: edits to the comments leave it unchanged, any code edit
+    changes it."""
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        cut = line.find("//")
+        while cut >= 0 and line.count('"', 0, cut) % 2:
+            cut = line.find("//", cut + 2)       # inside a string literal
+        code = (line[:cut] if cut >= 0 else line).rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def parse(argv=None):
@@ -312,9 +328,8 @@ def dominant_roofline(kernels, workload, peaks):
         roof["frac_of_measured_peak"] = roof["achieved"] / peaks[key]
     traffic = None
     src = os.path.join(ROOT, "fp8_block_quantized_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as fh:
-        same_source = hashlib.sha256(fh.read()).hexdigest() == TRAFFIC_SOURCE_SHA256
-    if workload == "dsv3" and same_source and name in TRAFFIC:
+    same_code = kernel_code_digest(src) == TRAFFIC_CODE_DIGEST
+    if workload == "dsv3" and same_code and name in TRAFFIC:
         traffic = float(sum(TRAFFIC[name]))
     roof.update({"kernel": name, "traffic": traffic, "traffic_unit": "bytes per launch",
                  "alg_bytes_per_launch": k["bytes"], "alg_flops_per_launch": k["flops"],

@@ -672,9 +672,9 @@ constexpr int kRingW = 256 * 128;      // 256 weight rows x one 128-byte K block
 // float scales would) and of the tile's 256 weight rows, loaded by waves 2-5
 // in the slots the other waves leave unused.
 //
-// As in GEMM1, a wave whose 64 token rows of the tile are all padding (its
-// first row is the sentinel) loads, waits and stores as usual but skips its
-// MFMAs.  The stores of a 16-row group that is all padding go to the 1 KB
+// A wave whose 64 token rows of the tile are all padding (its first row is
+// the sentinel) loads, waits and stores as usual but skips its MFMAs (the
+// prefill GEMM1 skips per 16-row group; here that cost more than it saved).  The stores of a 16-row group that is all padding go to the 1 KB
 // dump rather than to y: every wave still issues kPf2Stores per tile, which
 // the ring's counted waits rely on, but the padding rows cost no HBM writes.
 constexpr int kPf2Loads = 7;               // DMA instructions per wave per stage
@@ -1110,7 +1110,8 @@ __global__ __launch_bounds__(512) void moe_gemm1_pf_kernel(GemmArgs args) {
 // a token is a two-step butterfly over its four lanes.  Tile, ring and row
 // gather as in moe_gemm1_pf_kernel; the stage's exponent slots hold the 128
 // token rows' words (waves 0, 1) and the 256 weight rows' words (waves 2-5).
-// As there, a wave whose 64 token rows are all padding skips its MFMAs.
+// A wave whose 64 token rows are all padding skips its MFMAs (a per-16-row
+// skip as in moe_gemm1_pf_kernel did not pay off here).
 __global__ __launch_bounds__(512) void moe_gemm1_mx_kernel(GemmArgs args) {
   constexpr int BM = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kPf1Stages * kPf1Stage];

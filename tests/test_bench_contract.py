@@ -89,3 +89,22 @@ def test_sections_and_cpu_threads():
     assert bench.parse([]).sections == bench.SECTIONS
     n = bench.cpu_threads()
     assert 1 <= n <= len(os.sched_getaffinity(0))
+
+
+def test_kernel_code_digest_ignores_comments_only(tmp_path):
+    """The per-launch traffic figures stay valid across comment edits of the
+    kernel source and lapse with any code edit."""
+    src = "int f(int a) {  // add one\n  return a + 1;\n}\n"
+    a = tmp_path / "a.hip"
+    a.write_text(src)
+    b = tmp_path / "b.hip"
+    b.write_text("// a header comment\nint f(int a) {   \n\n  return a + 1;  // the same\n}\n")
+    c = tmp_path / "c.hip"
+    c.write_text(src.replace("+ 1", "+ 2"))
+    d = tmp_path / "d.hip"
+    d.write_text('const char* s = "a // b";\n')
+    e = tmp_path / "e.hip"
+    e.write_text('const char* s = "a // c";\n')
+    assert bench.kernel_code_digest(str(a)) == bench.kernel_code_digest(str(b))
+    assert bench.kernel_code_digest(str(a)) != bench.kernel_code_digest(str(c))
+    assert bench.kernel_code_digest(str(d)) != bench.kernel_code_digest(str(e))

@@ -154,8 +154,13 @@ def test_quant_fmt_full_size_workload(group, fmt):
 @pytest.mark.parametrize("T,E,k,renorm,kind", [
     (16, 8, 2, True, "normal"), (64, 256, 8, True, "bias"), (33, 128, 8, False, "normal"),
     (1, 128, 8, True, "normal"), (7, 5, 5, True, "normal"), (3, 1, 1, False, "normal"),
-    (8192, 256, 8, True, "bias"), (100, 512, 32, True, "normal"), (50, 60, 3, False, "ties")])
+    (8192, 256, 8, True, "bias"), (100, 512, 32, True, "normal"), (50, 60, 3, False, "ties"),
+    (64, 256, 32, True, "coarse"), (16, 512, 16, False, "equal"), (8, 128, 8, True, "signed_zero")])
 def test_router(T, E, k, renorm, kind):
+    """The selection's (value, index) order decides every tie: equal logits
+    in lanes of different 16-lane rows and register slots ("coarse": seven
+    distinct values over 256 experts; "equal": all logits equal, so the ids
+    are 0 .. k-1; "signed_zero": -0 and +0, which compare equal)."""
     note(f"router T={T} E={E} k={k} renorm={renorm} {kind}")
     g = torch.Generator().manual_seed(T * 1000 + E + k)
     logits = torch.randn((T, E), generator=g)
@@ -163,6 +168,12 @@ def test_router(T, E, k, renorm, kind):
         logits += 0.5 * (torch.randint(0, 2, (E,), generator=g) * 2 - 1)
     if kind == "ties":
         logits = torch.round(logits * 2) / 2       # many equal logits
+    if kind == "coarse":
+        logits = torch.round(logits).clamp(-3, 3)
+    if kind == "equal":
+        logits = torch.full((T, E), 0.25)
+    if kind == "signed_zero":
+        logits = torch.where(torch.rand((T, E), generator=g) < 0.5, torch.tensor(-0.0), torch.tensor(0.0))
     ids, w = moe.moe_topk_softmax(logits.cuda(), k, renorm)
     torch.cuda.synchronize()
     rids, rw = ref_router.topk_softmax(logits.numpy(), k, renorm)
