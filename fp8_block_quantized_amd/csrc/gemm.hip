@@ -327,9 +327,11 @@ __global__ __launch_bounds__(256) void moe_gemm2_kernel(GemmArgs args) {
 // |w2| * (one grid step), so the intermediate a must round to the same
 // float32 as the exact product would.  The FP8 MFMA sums its products
 // below float32 precision (about 1.4e-6 of sum |p| per 128 products on
-// gfx950), which moves ~0.5% of those codes; so this GEMM converts both e4m3
-// operands exactly to f16 (v_cvt_scalef32_pk_f16_fp8 with scale 1) and runs
-// v_mfma_f32_16x16x32_f16 (four per 128-wide K block, chained), whose float32
+// gfx950), which moved 0.16-0.5% of those codes on the Mixtral-, Qwen3- and
+// DeepSeek-shaped layers and took outputs past the layer's bar; so this GEMM
+// converts both e4m3 operands exactly to f16 (v_cvt_scalef32_pk_f16_fp8 with
+// scale 1) and runs v_mfma_f32_16x16x32_f16 (four per 128-wide K block,
+// chained), whose float32
 // accumulation of the exact 8-bit products is accurate to ~1e-10 of sum |p|.
 // Each block partial is scaled by xs * ws in float64 (exact) and summed in
 // float64, and SiLU*mul is evaluated in float64 before the one rounding of
